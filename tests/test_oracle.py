@@ -1,0 +1,373 @@
+"""Pins for the fp64 oracle: properties fixed by the mathematics of masked softmax attention,
+checked independently of the oracle's own loop (CPU only).
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped rope term, a wrong
+scale, a transposed or mis-offset mask, the wrong request segment, a wrong tie-break, V
+taken over the wrong dims) fails at least one test here.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import workloads as wl
+
+D, DL = wl.KV_DIM, wl.LATENT_DIM
+
+
+def f64(a):
+    a = np.asarray(a)
+    return wl.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def visibility(w, r):
+    """Dense [T_r, L_r] visibility: every prefix column, plus the tail columns of the mask."""
+    t, p = int(w.tree_lens[r]), int(w.prefix_lens[r])
+    l = t + p
+    m = w.custom_mask[w.mask_indptr[r]:w.mask_indptr[r + 1]].reshape(t, l)
+    vis = m != 0
+    vis[:, :p] = True
+    return vis
+
+
+def dense_reference(w, pool, dl=DL):
+    """Brute force: materialise S = scale*Q K^T, set invisible entries to -inf, then the
+    library softmax and logsumexp, then A @ V. Rows ordered (token, head)."""
+    h = w.num_heads
+    d = pool.shape[1]
+    outs, lses, ams = [], [], []
+    for r in range(w.bs):
+        t = int(w.tree_lens[r])
+        k = f64(pool[w.kv_indices[w.kv_indptr[r]:w.kv_indptr[r + 1]]])
+        qq = f64(w.q[w.qo_indptr[r]:w.qo_indptr[r + 1]]).reshape(t * h, d)
+        vis = np.repeat(visibility(w, r), h, axis=0)
+        s = w.scale * (qq @ k.T)
+        s = np.where(vis, s, -np.inf)
+        a = scipy.special.softmax(s, axis=1)
+        outs.append(a @ k[:, :dl])
+        lses.append(scipy.special.logsumexp(s, axis=1))
+        ams.append(np.argmax(s, axis=1))
+    return np.concatenate(outs), np.concatenate(lses), np.concatenate(ams)
+
+
+def run(w, pool=None, **kw):
+    return oracle.run_workload(w, pool=pool, **kw)
+
+
+def small(seed, bs=2, h=3, p=(5, 17), t=(3, 4), slots=256, in_dtype="bf16", tree="random"):
+    rng = np.random.default_rng(seed)
+    return wl.build_workload("t", rng, h, list(p)[:bs], list(t)[:bs], slots, in_dtype=in_dtype,
+                             tree=tree)
+
+
+# --------------------------------------------------------------------------- P1 brute force
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_fuzz(seed):
+    rng = np.random.default_rng(1000 + seed)
+    bs = int(rng.integers(1, 5))
+    h = int(rng.choice([1, 3, 8]))
+    t = rng.integers(1, 9, bs)
+    p = rng.integers(0, 201, bs)
+    in_dtype = "fp32" if seed % 3 == 0 else "bf16"
+    w = wl.build_workload("fuzz", rng, h, p, t, int((p + t).sum()) + 50, in_dtype=in_dtype)
+    pool = w.pool_np()
+    out, lse, am = run(w, pool)
+    ro, rl, ra = dense_reference(w, pool)
+    assert np.max(np.abs(out - ro)) <= 1e-12
+    assert np.max(np.abs(lse - rl) / np.maximum(1.0, np.abs(rl))) <= 1e-12
+    # argmax rows are reported as key positions within the request
+    assert np.array_equal(am, ra)
+
+
+def test_brute_force_small_dims():
+    """Dl and Dr are parameters of the definition: check a 4+2 dim case the same way."""
+    rng = np.random.default_rng(7)
+    dl, dr, h, p, t = 4, 2, 2, 6, 3
+    d = dl + dr
+    l = p + t
+    pool = rng.standard_normal((20, d)).astype(np.float32)
+    idx = rng.permutation(20)[:l].astype(np.int64)
+    q = rng.standard_normal((t, h, d)).astype(np.float32)
+    parents = np.array([-1, 0, 0])
+    mask = np.ones((t, l), np.uint8)
+    mask[:, p:] = wl.ancestor_or_self(parents)
+    out, lse, am = oracle.verify_attn(q, pool, idx, np.array([0, l], np.int32),
+                                      np.array([0, t], np.int64), mask.ravel(),
+                                      np.array([0, t * l], np.int64), h, 0.7, dl, dr)
+    k = pool[idx].astype(np.float64)
+    s = 0.7 * (q.reshape(t * h, d).astype(np.float64) @ k.T)
+    vis = np.repeat(mask != 0, h, axis=0)
+    s[~vis] = -np.inf
+    assert np.allclose(out, scipy.special.softmax(s, axis=1) @ k[:, :dl], atol=1e-14, rtol=0)
+    assert np.allclose(lse, scipy.special.logsumexp(s, axis=1), atol=1e-14, rtol=0)
+
+
+def test_brute_force_tiny_workload():
+    w = wl.tiny()
+    pool = w.pool_np()
+    out, lse, am = run(w, pool)
+    ro, rl, ra = dense_reference(w, pool)
+    assert np.max(np.abs(out - ro)) <= 1e-12
+    assert np.array_equal(am, ra)
+
+
+# --------------------------------------------------------------------------- P2 identical rows
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp32"])
+def test_identical_rows_return_that_row(in_dtype):
+    w = small(3, in_dtype=in_dtype)
+    w.kv_rows[:] = w.kv_rows[0]
+    out, lse, _ = run(w)
+    v = f64(w.kv_rows[0])[:DL]
+    assert np.array_equal(out, np.broadcast_to(v, out.shape))
+
+
+# --------------------------------------------------------------------------- P3 self only at P=0
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp32"])
+def test_self_only_at_zero_prefix(in_dtype):
+    rng = np.random.default_rng(11)
+    t, h = 5, 4
+    w = wl.build_workload("self", rng, h, [0], [t], 64, in_dtype=in_dtype)
+    w.custom_mask[:] = np.eye(t, dtype=np.uint8).ravel()
+    out, lse, am = run(w)
+    q, kv = f64(w.q), f64(w.kv_rows)
+    for i in range(t):
+        for hh in range(h):
+            n = i * h + hh
+            assert np.array_equal(out[n], kv[i, :DL])
+            score = w.scale * math.fsum(q[i, hh] * kv[i])
+            assert abs(lse[n] - score) <= 1e-14 * max(1.0, abs(score))
+            assert am[n] == i
+
+
+def test_single_token_tree_sees_prefix_and_itself():
+    """T=1 at P=0 with the mask bit set: the lone query attends only to its own key."""
+    rng = np.random.default_rng(5)
+    w = wl.build_workload("one", rng, 2, [0], [1], 8)
+    out, _, am = run(w)
+    assert np.array_equal(out[0], f64(w.kv_rows[0])[:DL])
+    assert np.all(am == 0)
+
+
+# --------------------------------------------------------------------------- P4 invariances
+def test_slot_relabel_is_bitwise_invariant():
+    w = small(21)
+    pool = w.pool_np()
+    out, lse, am = run(w, pool)
+    perm = np.random.default_rng(0).permutation(w.num_slots)
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    w.kv_indices = perm[w.kv_indices].astype(np.int64)
+    out2, lse2, am2 = run(w, pool2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2) and np.array_equal(am, am2)
+
+
+def test_prefix_permutation_invariance():
+    w = small(22, bs=1, p=(40,), t=(4,))
+    pool = w.pool_np()
+    out, lse, am = run(w, pool)
+    p = int(w.prefix_lens[0])
+    perm = np.random.default_rng(1).permutation(p)
+    w.kv_indices[:p] = w.kv_indices[:p][perm]
+    out2, lse2, am2 = run(w, pool)
+    assert np.max(np.abs(out - out2)) <= 1e-13
+    assert np.max(np.abs(lse - lse2)) <= 1e-13
+    # the argmax key moves with the permutation (prefix winners) or stays (tree winners)
+    inv = np.argsort(perm)
+    expect = np.where(am < p, inv[np.minimum(am, p - 1)], am)
+    assert np.array_equal(am2, expect)
+
+
+def test_tree_node_permutation_equivariance():
+    w = small(23, bs=1, p=(30,), t=(6,), h=2)
+    pool = w.pool_np()
+    out, lse, am = run(w, pool)
+    t, p, h = 6, 30, 2
+    l = t + p
+    sig = np.random.default_rng(2).permutation(t)    # new node k is old node sig[k]
+    m = w.custom_mask.reshape(t, l)
+    tail = m[:, p:][sig][:, sig]
+    m2 = np.concatenate([m[sig][:, :p], tail], axis=1)
+    w.custom_mask = np.ascontiguousarray(m2.ravel())
+    w.q = np.ascontiguousarray(w.q[sig])
+    w.kv_indices[p:] = w.kv_indices[p:][sig]
+    out2, lse2, am2 = run(w, pool)
+    old_rows = (sig[:, None] * h + np.arange(h)[None, :]).ravel()
+    assert np.max(np.abs(out2 - out[old_rows])) <= 1e-13
+    assert np.max(np.abs(lse2 - lse[old_rows])) <= 1e-13
+    inv = np.argsort(sig)
+    a = am[old_rows]
+    assert np.array_equal(am2, np.where(a < p, a, p + inv[np.maximum(a - p, 0)]))
+
+
+def test_prefix_mask_columns_and_invisible_rows_are_ignored():
+    w = small(24, bs=2, p=(12, 9), t=(5, 4))
+    # hide the last tree node of each request from every query, itself included
+    hidden = []
+    for r in range(w.bs):
+        t, p = int(w.tree_lens[r]), int(w.prefix_lens[r])
+        m = w.custom_mask[w.mask_indptr[r]:w.mask_indptr[r + 1]].reshape(t, t + p)
+        m[:, p + t - 1] = 0
+        hidden.append(int(w.kv_indices[w.kv_indptr[r] + p + t - 1]))
+    pool = w.pool_np()
+    out, lse, am = run(w, pool)
+    # random prefix columns of the mask, and garbage in the hidden keys' pool rows
+    rng = np.random.default_rng(3)
+    for r in range(w.bs):
+        t, p = int(w.tree_lens[r]), int(w.prefix_lens[r])
+        m = w.custom_mask[w.mask_indptr[r]:w.mask_indptr[r + 1]].reshape(t, t + p)
+        m[:, :p] = rng.integers(0, 2, (t, p))
+    pool2 = pool.copy()
+    pool2[hidden] = wl.to_bf16_bits(np.full((len(hidden), D), 1e4, np.float32))
+    out2, lse2, am2 = run(w, pool2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2) and np.array_equal(am, am2)
+
+
+def test_nonzero_mask_bytes_mean_visible():
+    w = small(25)
+    out, lse, am = run(w)
+    w.custom_mask = np.where(w.custom_mask != 0, np.uint8(0xA5), np.uint8(0))
+    out2, lse2, am2 = run(w)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_mask_is_indexed_by_global_key_position_and_request():
+    """Hiding one tree key from one query changes exactly that query's rows."""
+    w = small(26, bs=2, p=(7, 11), t=(4, 5), h=2)
+    out, lse, _ = run(w)
+    r, i = 1, 3
+    t, p = int(w.tree_lens[r]), int(w.prefix_lens[r])
+    m = w.custom_mask[w.mask_indptr[r]:w.mask_indptr[r + 1]].reshape(t, t + p)
+    k = int(np.nonzero(m[i, p:p + i])[0][0]) if m[i, p:p + i].any() else i
+    m[i, p + k] = 0
+    out2, lse2, _ = run(w)
+    changed = np.nonzero(np.any(out != out2, axis=1))[0]
+    tok = int(w.qo_indptr[r]) + i
+    assert set(changed.tolist()) == {tok * 2, tok * 2 + 1}
+
+
+# --------------------------------------------------------------------------- P5 closed forms
+def test_zero_query_gives_mean_of_visible_values():
+    w = small(31, bs=2, p=(10, 3), t=(4, 6), h=2)
+    w.q[:] = 0
+    out, lse, am = run(w)
+    kv = f64(w.kv_rows)
+    n = 0
+    for r in range(w.bs):
+        vis = visibility(w, r)
+        base = int(w.kv_indptr[r])
+        for i in range(int(w.tree_lens[r])):
+            cols = np.nonzero(vis[i])[0]
+            mean = kv[base + cols, :DL].mean(axis=0)
+            for _ in range(w.num_heads):
+                assert np.max(np.abs(out[n] - mean)) <= 1e-15
+                assert abs(lse[n] - math.log(len(cols))) <= 1e-15
+                assert am[n] == cols[0]       # all scores tie at 0: the smallest position
+                n += 1
+
+
+def test_two_visible_keys_closed_form():
+    rng = np.random.default_rng(32)
+    w = wl.build_workload("two", rng, 3, [1], [1], 16, in_dtype="fp32")
+    out, lse, am = run(w)
+    q, kv = f64(w.q)[0], f64(w.kv_rows)
+    for hh in range(3):
+        s1 = w.scale * math.fsum(q[hh] * kv[0])
+        s2 = w.scale * math.fsum(q[hh] * kv[1])
+        e = math.exp(s2 - s1)
+        ref = (kv[0, :DL] + e * kv[1, :DL]) / (1.0 + e)
+        assert np.max(np.abs(out[hh] - ref)) <= 1e-14
+        assert abs(lse[hh] - (s1 + math.log1p(e))) <= 1e-13
+        assert am[hh] == (0 if s1 >= s2 else 1)
+
+
+def test_duplicate_slots_are_separate_keys_and_ties_break_low():
+    """Two positions holding the same slot tie exactly; argmax takes the lower position and
+    the duplicated key counts twice in the softmax."""
+    rng = np.random.default_rng(33)
+    w = wl.build_workload("dup", rng, 2, [3], [1], 16, in_dtype="fp32")
+    w.kv_indices[2] = w.kv_indices[0]
+    pool = w.pool_np()
+    pool[w.kv_indices[0]] = 0.5 * np.sign(w.q[0, 0])    # key 0 (and 2) wins for head 0
+    out, lse, am = run(w, pool)
+    assert am[0] == 0
+    k = pool[w.kv_indices].astype(np.float64)
+    s = w.scale * (f64(w.q)[0, 0] @ k.T)
+    wgt = np.exp(s - s.max())
+    assert np.max(np.abs(out[0] - (wgt @ k[:, :DL]) / wgt.sum())) <= 1e-14
+
+
+def test_empty_visible_set():
+    rng = np.random.default_rng(34)
+    w = wl.build_workload("empty", rng, 2, [0], [3], 16)
+    w.custom_mask[:] = 0
+    w.custom_mask.reshape(3, 3)[1, 1] = 1        # only token 1 sees anything
+    out, lse, am = run(w)
+    for n in (0, 1, 4, 5):
+        assert np.all(out[n] == 0) and lse[n] == -np.inf and am[n] == -1
+    assert np.array_equal(out[2], f64(w.kv_rows[1])[:DL]) and am[2] == 1
+
+
+# --------------------------------------------------------------------------- P6 rope shift
+def test_rope_shift_invariance():
+    w = small(41, bs=1, p=(20,), t=(3,), h=2, in_dtype="fp32")
+    pool = w.pool_np()
+    # rope dims on a 2^-8 grid so that the shift below is exact in float32
+    pool[w.kv_indices, DL:] = np.round(pool[w.kv_indices, DL:] * 256) / 256
+    out, lse, am = run(w, pool)
+    u = np.round(np.random.default_rng(4).standard_normal(D - DL) * 64).astype(np.float32) / 256
+    pool2 = pool.copy()
+    pool2[w.kv_indices, DL:] += u
+    out2, lse2, am2 = run(w, pool2)
+    assert np.max(np.abs(out - out2)) <= 1e-12
+    q = f64(w.q)
+    shift = np.array([w.scale * (q[t, hh, DL:] @ (pool2[w.kv_indices[0], DL:].astype(np.float64)
+                                                   - pool[w.kv_indices[0], DL:]))
+                      for t in range(3) for hh in range(2)])
+    assert np.max(np.abs((lse2 - lse) - shift)) <= 1e-11
+    assert np.array_equal(am, am2)
+
+
+def test_latent_is_the_value_and_rope_only_scores():
+    """Changing only rope dims of a key moves scores but never appears in out directly:
+    with a single visible key out equals the first 512 dims whatever the rope holds."""
+    rng = np.random.default_rng(42)
+    w = wl.build_workload("lat", rng, 1, [0], [1], 4, in_dtype="fp32")
+    pool = w.pool_np()
+    pool[w.kv_indices[0], DL:] = 123.0
+    out, lse, _ = run(w, pool)
+    assert np.array_equal(out[0], pool[w.kv_indices[0], :DL].astype(np.float64))
+
+
+# --------------------------------------------------------------------------- rows subset
+def test_row_subset_matches_full():
+    w = small(51, bs=3, p=(5, 0, 9), t=(2, 3, 1), h=3)
+    out, lse, am = run(w)
+    rows = np.array([8, 0, 17, 5, 3])
+    o2, l2, a2 = run(w, rows=rows)
+    assert np.array_equal(o2, out[rows]) and np.array_equal(l2, lse[rows])
+
+
+def test_thread_count_does_not_change_results():
+    w = small(52, bs=2, p=(60, 33), t=(4, 7), h=4)
+    a = run(w, nthreads=1)
+    b = run(w, nthreads=4)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# --------------------------------------------------------------------------- error paths
+def test_negative_prefix_is_rejected():
+    w = small(61)
+    w.kv_indptr = np.array([0, 2, 2 + int(w.kv_indptr[2] - w.kv_indptr[1])], np.int32)
+    with pytest.raises(oracle.OracleError):
+        run(w)
+
+
+def test_out_of_range_slot_is_rejected():
+    w = small(62)
+    pool = w.pool_np()
+    w.kv_indices[3] = w.num_slots
+    with pytest.raises(oracle.OracleError):
+        run(w, pool)
