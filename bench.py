@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA tree-verify attention step on one MI355X.
+
+A step is one verify_attn_run over the whole batch (split-K partial kernel + combine). The
+default workload is the long-context one: 1 request, H=64 heads, a 23,000-key prefix and a
+16-node random draft tree, bf16 q [16,64,576] and a bf16 latent cache scattered over a
+1,048,576-slot pool. Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout. Everything else goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify-attn µs/step + effective HBM GB/s at P=23k, T=16, H=64 (% roofline)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w, out_bytes=4):
+    """Bytes the method must move and flops it must do (one step)."""
+    e_in = 2 if w.in_dtype == "bf16" else 4
+    by = 0
+    fl = 0
+    for r in range(w.bs):
+        t, p = int(w.tree_lens[r]), int(w.prefix_lens[r])
+        l = t + p
+        by += l * (576 * e_in + 8) + t * w.num_heads * (576 * e_in + 512 * out_bytes) + t * t
+        m = w.custom_mask[w.mask_indptr[r]:w.mask_indptr[r + 1]].reshape(t, l)
+        vis_tree = int((m[:, p:] != 0).sum())
+        fl += 2 * (576 + 512) * w.num_heads * (t * p + vis_tree)
+    by += (w.bs + 1) * 20
+    return by, fl
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch uses (same process-wide copy)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime)
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.rt.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        rc = self.rt.hipEventElapsedTime(ctypes.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(f.value)
+
+    def destroy(self, e):
+        self.rt.hipEventDestroy(e)
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle on the host cores: a bounded, deterministic sample of rows, scaled to a
+    whole step."""
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    total = w.num_tokens * w.num_heads
+    pool = w.pool_np()
+    probe = np.arange(0, total, max(1, total // 32))[:32]
+    t0 = time.perf_counter()
+    oracle.run_workload(w, rows=probe, nthreads=cores, pool=pool)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(min(total, max(len(probe), budget_s / max(per_row, 1e-9))))
+    rows = np.linspace(0, total - 1, n).round().astype(np.int64)
+    rows = np.unique(rows)
+    t0 = time.perf_counter()
+    oracle.run_workload(w, rows=rows, nthreads=cores, pool=pool)
+    dt = time.perf_counter() - t0
+    us_step = dt / len(rows) * total * 1e6
+    return {"value": us_step, "unit": "us/step", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {total} (token, head) rows of the same workload, evenly "
+                      f"spaced, fp64 two-pass C loop with OpenMP; {dt:.2f} s wall, scaled to "
+                      f"all rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long",
+                    choices=["tiny", "short", "long", "segmented", "stress"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "simple", "mfma"])
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=50)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the verify path is a single-GPU kernel library "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from mla_tree_verify_paged_amd import VerifyAttn
+    from mla_tree_verify_paged_amd.binding import verify_attn_set_profiling_events
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+
+    w = workloads.make(args.workload)
+    log(f"workload {w.name}: bs={w.bs} H={w.num_heads} P={w.prefix_lens.tolist()} "
+        f"T={w.tree_lens.tolist()} in={w.in_dtype}")
+    dev = to_device(w)
+    va = VerifyAttn(w.num_heads, in_dtype=w.in_dtype, out_dtype="fp32", max_batch=w.bs,
+                    max_q_per_req=w.max_q_per_req, max_q_tokens=w.num_tokens,
+                    num_splits=args.splits, kernel=args.kernel)
+    info = va.info
+    kernel_name = {1: "simple", 2: "mfma"}[info.kernel]
+    log(f"kernel={kernel_name} splits={info.num_splits} workspace={info.workspace_bytes}")
+    out = torch.empty((w.num_tokens, w.num_heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.num_tokens, w.num_heads), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"],
+               dev["qo_indptr"], dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse,
+               None, bs=w.bs, num_tokens=w.num_tokens, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    status = va.read_device_status()
+    if status != 0 or not torch.isfinite(out).all():
+        log(f"bad output: status={status}")
+        sys.exit(1)
+
+    # ---- timed region: K eager steps, per-kernel HIP events recorded by the library
+    hev = HipEvents()
+    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        verify_attn_set_profiling_events(va.ctx, *e)
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    verify_attn_set_profiling_events(va.ctx, None, None, None)
+    part_ms = np.array([hev.elapsed_ms(a, b) for a, b, _ in evs])
+    comb_ms = np.array([hev.elapsed_ms(b, c) for _, b, c in evs])
+    for e in evs:
+        for x in e:
+            hev.destroy(x)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    log(f"eager: {ms_per_step * 1e3:.2f} us/step; partial {part_ms.mean() * 1e3:.2f} us, "
+        f"combine {comb_ms.mean() * 1e3:.2f} us")
+
+    # ---- graph replays (capture-safe path), warm and cold
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step_stream = s.cuda_stream
+        va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"],
+               dev["qo_indptr"], dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse,
+               None, bs=w.bs, num_tokens=w.num_tokens, stream=step_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"],
+               dev["qo_indptr"], dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse,
+               None, bs=w.bs, num_tokens=w.num_tokens,
+               stream=torch.cuda.current_stream().cuda_stream)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) * 1e6 / args.steps
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    cold = []
+    for _ in range(args.cold_steps):
+        flush.fill_(1.0)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        cold.append(a.elapsed_time(b) * 1e3)
+    cold = np.array(cold)
+    del flush
+    log(f"graph warm {graph_us:.2f} us/step; cold median {np.median(cold):.2f} us")
+
+    by, fl = algorithmic_work(w)
+    part_s = part_ms.mean() * 1e-3
+    us = ms_per_step * 1e3
+    achieved = fl / part_s / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: bs={w.bs}, H={w.num_heads}, P={w.prefix_lens.tolist()}, "
+                        f"T={w.tree_lens.tolist()} random draft trees, {w.in_dtype} absorbed q "
+                        f"[num_tok,H,576] and paged latent KV [{w.num_slots},576]",
+            "kernel": kernel_name,
+            "num_splits": int(info.num_splits),
+            "out_dtype": "fp32",
+        },
+        "effective_GBps": round(by / (us * 1e-6) / 1e9, 2),
+        "frac_hbm": round(by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "frac_mfma_step": round(fl / (us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+        "algorithmic_bytes": int(by),
+        "algorithmic_flops": int(fl),
+        "partial_kernel_us": round(part_ms.mean() * 1e3, 3),
+        "combine_kernel_us": round(comb_ms.mean() * 1e3, 3),
+        "graph_warm_us_per_step": round(graph_us, 3),
+        "graph_cold_us": {"median": round(float(np.median(cold)), 3),
+                          "p10": round(float(np.percentile(cold, 10)), 3),
+                          "p90": round(float(np.percentile(cold, 90)), 3)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "kernel": f"{kernel_name} partial (split-K)",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.0f} us/step")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

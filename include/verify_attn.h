@@ -1,0 +1,168 @@
+/*
+ * verify_attn.h - C ABI of the MI355X (gfx950) MLA tree-verify attention library.
+ *
+ * The operation (sources by page title and section):
+ *   Multi-head latent attention for verifying a speculative draft tree. Every draft-tree
+ *   query token, for every head, attends over a paged latent KV cache reached through slot
+ *   indices, under a mask made of a prefix length plus a tree visibility matrix, and returns
+ *   a 512-wide latent output row.
+ *   - absorbed q [num_tok, H, 576] and paged KV [num_slots, 576] = 512 latent + 64 rope:
+ *     "The Glue That Binds: Wiring a Custom CUDA Kernel into Production via C-ABI",
+ *     section "The Broader Engineering Effort";
+ *   - the latent kv_c is one 512-d vector per token shared by every head:
+ *     "The Glue That Connects: Wiring a Custom Flash Attention Kernel into the C-ABI Layer",
+ *     section "The Context: Building a Blackwell-Specific Verify Attention Kernel";
+ *   - prefix-length-plus-visibility mask, split-K flash decode, paged reads by slot:
+ *     "The Glue That Makes Kernels Run: A Study in Architectural Discipline",
+ *     section "The Context: A Custom Kernel in Flight";
+ *   - the mask indexed by the global key position, masked scores -inf:
+ *     "The Glue That Connects", section "Design Decisions and Trade-Offs";
+ *   - buffer dtypes (int64 kv_indices / qo_indptr / mask_indptr / out_cache_loc, int32
+ *     kv_indptr, uint8 custom_mask), scalars bs, q_len, H, Dl, Dr, scale and a fixed split
+ *     count, a caller workspace, no host synchronisation or allocation inside the call:
+ *     "The Final Solder Joint: Updating the C-ABI Layer for CUDA Graph Capture-Safety",
+ *     sections "The Investigation", "The Three-Edits Sequence", "Why the C-ABI Edit Matters"
+ *     and "Assumptions and Design Decisions".
+ *
+ * Per request r (T_r = qo_indptr[r+1]-qo_indptr[r] tree tokens, L_r = kv_indptr[r+1]-
+ * kv_indptr[r] keys, P_r = L_r - T_r prefix keys), tree token i, head h:
+ *   key j (0 <= j < L_r) lives in slot kv_indices[kv_indptr[r] + j]; the last T_r keys are
+ *   the tree tokens in query order; key j is visible iff j < P_r or
+ *   custom_mask[mask_indptr[r] + i*L_r + j] != 0 (prefix columns are never read);
+ *   s_j = sm_scale * <q[t,h,0:576], kv[slot_j,0:576]>,  t = qo_indptr[r] + i;
+ *   out[t,h,0:512] = sum_j softmax(s)_j * kv[slot_j, 0:512] over the visible keys;
+ *   out_lse[t,h] = natural-log sum-exp of the visible s_j;
+ *   out_argmax[t,h] = the smallest visible key position j with the largest s_j.
+ *   A row with no visible key gets out = 0, lse = -inf, argmax = -1.
+ *
+ * Conventions
+ *   Ownership: every tensor argument is caller-owned device memory. The library owns the
+ *     context and, only when the config brings no workspace, a workspace it allocates in
+ *     verify_attn_create (outside any stream capture) and frees in verify_attn_destroy.
+ *   Errors: functions return va_status; no exception or abort crosses the ABI. The message
+ *     of the last failure on the calling thread is verify_attn_last_error().
+ *   Bad device data (a slot outside [0, num_slots), L_r < T_r, T_r above max_q_per_req,
+ *     offsets outside the buffers) never leads to an out-of-bounds access: the offending
+ *     key is treated as invisible or the request's rows are written as empty rows, and a
+ *     sticky bit is set in a status word read by verify_attn_read_device_status.
+ *   Capture: verify_attn_run only enqueues kernels on `stream`; it allocates nothing,
+ *     copies nothing and never synchronises, so it may be recorded into a hipGraph. The
+ *     grid depends only on bs and the context's fixed configuration.
+ *   Concurrency: calls on one context must not overlap in time (the workspace is shared);
+ *     use one context per concurrently used stream.
+ *   Streams are passed as `void*` holding a hipStream_t (NULL = the default stream).
+ */
+#ifndef VERIFY_ATTN_H
+#define VERIFY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct verify_attn_ctx verify_attn_ctx;
+
+typedef enum {
+  VA_OK = 0,
+  VA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+  VA_ERR_INVALID = 2,     /* a scalar is out of range or inconsistent with the config      */
+  VA_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement                */
+  VA_ERR_WORKSPACE = 4,   /* the caller's workspace is too small or misaligned            */
+  VA_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed                   */
+} va_status;
+
+/* element types of q and kv_buffer (in_dtype) and of out (out_dtype) */
+enum { VA_BF16 = 0, VA_FP32 = 1 };
+
+/* kernel family: AUTO picks MFMA for bf16 inputs and the simple fp32 kernel otherwise */
+enum { VA_KERNEL_AUTO = 0, VA_KERNEL_SIMPLE = 1, VA_KERNEL_MFMA = 2 };
+
+/* sticky device status bits (verify_attn_read_device_status) */
+enum {
+  VA_DEV_SLOT_RANGE = 1u,  /* a kv_indices entry outside [0, num_slots): key ignored        */
+  VA_DEV_SEGMENT = 2u,     /* L_r < T_r, or offsets outside kv_indices / mask / q: rows empty */
+  VA_DEV_Q_PER_REQ = 4u,   /* T_r > max_q_per_req: the request's rows written empty         */
+  VA_DEV_TOKENS = 8u       /* qo_indptr[bs] != num_tokens: uncovered rows written empty     */
+};
+
+typedef struct {
+  int32_t num_heads;      /* H >= 1                                                        */
+  int32_t latent_dim;     /* Dl: must be 512                                               */
+  int32_t rope_dim;       /* Dr: must be 64                                                */
+  int32_t in_dtype;       /* VA_BF16 or VA_FP32 (q and kv_buffer)                          */
+  int32_t out_dtype;      /* VA_FP32 or VA_BF16 (out)                                      */
+  int32_t max_batch;      /* upper bound on bs                                             */
+  int32_t max_q_per_req;  /* upper bound on T_r                                            */
+  int64_t max_q_tokens;   /* upper bound on num_tokens                                     */
+  int32_t num_splits;     /* key splits per request (1..256); 0 = chosen from the bounds    */
+  int32_t kernel;         /* VA_KERNEL_*                                                   */
+  void *workspace;        /* device memory, 256-byte aligned, or NULL: allocated at create */
+  size_t workspace_bytes; /* size of `workspace` when it is not NULL                        */
+} verify_attn_config;
+
+typedef struct {
+  int32_t kernel;         /* the kernel family actually used                              */
+  int32_t num_splits;     /* the split count fixed for the context's life                 */
+  int32_t rows_per_block; /* (token, head) rows handled by one partial workgroup           */
+  int32_t row_tiles_per_req; /* row tiles per request in the launch grid                   */
+  size_t workspace_bytes; /* bytes of workspace in use                                     */
+} verify_attn_info;
+
+/* Workspace bytes a config needs (0 if the config is invalid). */
+size_t verify_attn_workspace_bytes(const verify_attn_config *cfg);
+
+/* Validates `cfg`, binds or allocates the workspace, clears the status word (synchronously,
+ * on the null stream). Returns VA_OK and sets *out, or an error and leaves *out NULL. */
+va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **out);
+
+/*
+ * Enqueues one verify step on `stream`.
+ *   q            [num_tokens, H, 576] in_dtype, contiguous.
+ *   kv_buffer    [num_slots, 576] in_dtype, contiguous rows (the paged latent cache).
+ *   kv_indices   int64 [num_kv_indices]: per request P_r prefix slots then T_r tree slots.
+ *   kv_indptr    int32 [bs+1], non-decreasing, kv_indptr[bs] <= num_kv_indices.
+ *   qo_indptr    int64 [bs+1], non-decreasing, qo_indptr[bs] == num_tokens.
+ *   custom_mask  uint8 [mask_len]: request r's [T_r, L_r] row-major matrix at mask_indptr[r].
+ *   mask_indptr  int64 [bs+1] element offsets into custom_mask.
+ *   out_cache_loc must be NULL (tree slots come from the tail of each kv_indices segment).
+ *   out          [num_tokens, H, 512] out_dtype.
+ *   out_lse      nullable float [num_tokens, H].
+ *   out_argmax   nullable int32 [num_tokens, H].
+ * Host-checked: pointers, 0 <= bs <= max_batch, 0 <= num_tokens <= max_q_tokens, finite
+ * sm_scale, num_slots >= 1. Returns VA_ERR_HIP if a launch fails.
+ */
+va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_buffer,
+                          int64_t num_slots, const int64_t *kv_indices, int64_t num_kv_indices,
+                          const int32_t *kv_indptr, const int64_t *qo_indptr,
+                          const uint8_t *custom_mask, int64_t mask_len,
+                          const int64_t *mask_indptr, const int64_t *out_cache_loc, int32_t bs,
+                          int64_t num_tokens, float sm_scale, void *out, float *out_lse,
+                          int32_t *out_argmax, void *stream);
+
+/* Synchronises `stream`, returns the sticky VA_DEV_* bits in *flags and clears them.
+ * Never call it inside a stream capture. */
+va_status verify_attn_read_device_status(verify_attn_ctx *ctx, void *stream, uint32_t *flags);
+
+/* Profiling: when set (non-NULL hipEvent_t handles passed as void*), every later
+ * verify_attn_run records `before` ahead of the partial kernel, `between` after it and
+ * `after` after the combine kernel, on the run's stream. Pass NULLs to stop. Not for use
+ * while the stream is being captured. */
+va_status verify_attn_set_profiling_events(verify_attn_ctx *ctx, void *before, void *between,
+                                           void *after);
+
+/* Reports the fixed launch configuration of a context. */
+va_status verify_attn_get_info(const verify_attn_ctx *ctx, verify_attn_info *info);
+
+/* Frees the context and any workspace it allocated. NULL is a no-op. */
+void verify_attn_destroy(verify_attn_ctx *ctx);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *verify_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_ATTN_H */

@@ -1,0 +1,297 @@
+// capi.cpp - the extern "C" boundary declared in include/verify_attn.h.
+//
+// The pages' C-ABI shim takes device pointers and a stream, computes the grid itself,
+// returns error codes ("The Glue That Connects", sections "What the Edit Actually Does" and
+// "Assumptions Embedded in the Integration"; "The Glue That Makes Kernels Run", section "The
+// Subject Message"), consumes the serving framework's native buffers directly and does no
+// host-side preprocessing or synchronisation ("The Final Solder Joint", sections "Why the
+// C-ABI Edit Matters" and "Assumptions and Design Decisions"). The pages' earlier version
+// allocated its workspace with a raw device malloc on first use, which broke graph capture
+// ("The Final Solder Joint", section "The Capture-Safety Constraint"); here the workspace is
+// bound once at create and run() only enqueues kernels.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "../../include/verify_attn.h"
+#include "va_internal.h"
+
+struct verify_attn_ctx {
+  verify_attn_config cfg;
+  int32_t kernel;
+  int32_t splits;
+  int32_t rows_per_block;
+  int32_t row_tiles_per_req;
+  size_t ws_bytes;
+  void *ws_base;
+  bool ws_owned;
+  va::Workspace ws;
+  hipEvent_t ev[3];  // profiling events (all NULL when off)
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+va_status fail(va_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+va_status ok() {
+  g_last_error.clear();
+  return VA_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Checks a config and fills the derived launch parameters. Returns VA_OK or an error.
+va_status derive(const verify_attn_config *c, int32_t *kernel, int32_t *splits,
+                 int32_t *rows_per_block, int32_t *row_tiles, size_t *bytes) {
+  if (!c) return fail(VA_ERR_NULL, "config is NULL");
+  if (c->num_heads < 1 || c->num_heads > 4096)
+    return fail(VA_ERR_INVALID, "num_heads %d out of range [1, 4096]", c->num_heads);
+  if (c->latent_dim != va::kLatent || c->rope_dim != va::kRope)
+    return fail(VA_ERR_UNSUPPORTED, "latent_dim/rope_dim must be 512/64 (got %d/%d)",
+                c->latent_dim, c->rope_dim);
+  if (c->in_dtype != VA_BF16 && c->in_dtype != VA_FP32)
+    return fail(VA_ERR_INVALID, "in_dtype %d unknown", c->in_dtype);
+  if (c->out_dtype != VA_BF16 && c->out_dtype != VA_FP32)
+    return fail(VA_ERR_INVALID, "out_dtype %d unknown", c->out_dtype);
+  if (c->max_batch < 1 || c->max_q_per_req < 1 || c->max_q_tokens < 1)
+    return fail(VA_ERR_INVALID, "max_batch, max_q_per_req and max_q_tokens must be >= 1");
+  if (c->max_q_per_req > 65536 || c->max_q_tokens > (int64_t(1) << 26))
+    return fail(VA_ERR_INVALID, "max_q_per_req or max_q_tokens too large");
+  if (c->num_splits < 0 || c->num_splits > va::kMaxSplits)
+    return fail(VA_ERR_INVALID, "num_splits %d out of range [0, %d]", c->num_splits,
+                va::kMaxSplits);
+  int32_t k = c->kernel;
+  if (k == VA_KERNEL_AUTO) k = c->in_dtype == VA_BF16 ? VA_KERNEL_MFMA : VA_KERNEL_SIMPLE;
+  if (k != VA_KERNEL_SIMPLE && k != VA_KERNEL_MFMA)
+    return fail(VA_ERR_INVALID, "kernel %d unknown", c->kernel);
+  if (k == VA_KERNEL_MFMA && c->in_dtype != VA_BF16)
+    return fail(VA_ERR_UNSUPPORTED, "the MFMA kernel takes bf16 inputs only");
+
+  int32_t rpb, tiles;
+  int64_t blocks_per_split;
+  if (k == VA_KERNEL_SIMPLE) {
+    rpb = va::kSimpleHeadsPerBlock;
+    tiles = int32_t(int64_t(c->max_q_per_req) * ceil_div(c->num_heads, rpb));
+  } else {
+    rpb = va::kMfmaRowsPerBlock;
+    tiles = int32_t(ceil_div(int64_t(c->max_q_per_req) * c->num_heads, rpb));
+  }
+  blocks_per_split = int64_t(c->max_batch) * tiles;
+  int32_t s = c->num_splits;
+  if (s == 0) {
+    // enough workgroups to cover the 256 compute units once (MFMA) or several times
+    const int64_t target = k == VA_KERNEL_MFMA ? 256 : 2048;
+    s = int32_t(ceil_div(target, blocks_per_split));
+    if (s < 1) s = 1;
+    if (s > 64) s = 64;
+  }
+  if (blocks_per_split * s > 0x7fffffffLL)
+    return fail(VA_ERR_INVALID, "launch grid too large");
+  const int64_t rows_cap = c->max_q_tokens * c->num_heads;
+  size_t off[5];
+  *bytes = va::workspace_layout(s, rows_cap, off);
+  *kernel = k;
+  *splits = s;
+  *rows_per_block = rpb;
+  *row_tiles = tiles;
+  return VA_OK;
+}
+
+void bind_workspace(verify_attn_ctx *x) {
+  size_t off[5];
+  const int64_t rows_cap = x->cfg.max_q_tokens * x->cfg.num_heads;
+  va::workspace_layout(x->splits, rows_cap, off);
+  char *b = static_cast<char *>(x->ws_base);
+  x->ws.status = reinterpret_cast<uint32_t *>(b + off[0]);
+  x->ws.part_o = reinterpret_cast<float *>(b + off[1]);
+  x->ws.part_lse = reinterpret_cast<float *>(b + off[2]);
+  x->ws.part_max = reinterpret_cast<float *>(b + off[3]);
+  x->ws.part_arg = reinterpret_cast<int32_t *>(b + off[4]);
+  x->ws.rows_cap = rows_cap;
+  x->ws.splits = x->splits;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t verify_attn_workspace_bytes(const verify_attn_config *cfg) {
+  int32_t k, s, rpb, tiles;
+  size_t bytes = 0;
+  if (derive(cfg, &k, &s, &rpb, &tiles, &bytes) != VA_OK) return 0;
+  return bytes;
+}
+
+va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **out) {
+  if (!out) return fail(VA_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  int32_t k, s, rpb, tiles;
+  size_t bytes = 0;
+  va_status st = derive(cfg, &k, &s, &rpb, &tiles, &bytes);
+  if (st != VA_OK) return st;
+  void *base = cfg->workspace;
+  bool owned = false;
+  if (base) {
+    if (cfg->workspace_bytes < bytes)
+      return fail(VA_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed",
+                  cfg->workspace_bytes, bytes);
+    if (reinterpret_cast<uintptr_t>(base) & 255)
+      return fail(VA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  } else {
+    hipError_t e = hipMalloc(&base, bytes);
+    if (e != hipSuccess)
+      return fail(VA_ERR_HIP, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+    owned = true;
+  }
+  hipError_t e = hipMemset(base, 0, 256);  // status word
+  if (e != hipSuccess) {
+    if (owned) (void)hipFree(base);
+    return fail(VA_ERR_HIP, "hipMemset failed: %s", hipGetErrorString(e));
+  }
+  auto *x = new (std::nothrow) verify_attn_ctx();
+  if (!x) {
+    if (owned) (void)hipFree(base);
+    return fail(VA_ERR_INVALID, "out of host memory");
+  }
+  x->cfg = *cfg;
+  x->kernel = k;
+  x->splits = s;
+  x->rows_per_block = rpb;
+  x->row_tiles_per_req = tiles;
+  x->ws_bytes = bytes;
+  x->ws_base = base;
+  x->ws_owned = owned;
+  x->ev[0] = x->ev[1] = x->ev[2] = nullptr;
+  bind_workspace(x);
+  *out = x;
+  return ok();
+}
+
+va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_buffer,
+                          int64_t num_slots, const int64_t *kv_indices, int64_t num_kv_indices,
+                          const int32_t *kv_indptr, const int64_t *qo_indptr,
+                          const uint8_t *custom_mask, int64_t mask_len,
+                          const int64_t *mask_indptr, const int64_t *out_cache_loc, int32_t bs,
+                          int64_t num_tokens, float sm_scale, void *out, float *out_lse,
+                          int32_t *out_argmax, void *stream) {
+  if (!ctx) return fail(VA_ERR_NULL, "ctx is NULL");
+  if (out_cache_loc)
+    return fail(VA_ERR_UNSUPPORTED, "out_cache_loc is not supported: pass NULL and keep the "
+                                    "tree slots at the tail of each kv_indices segment");
+  if (bs < 0 || bs > ctx->cfg.max_batch)
+    return fail(VA_ERR_INVALID, "bs %d out of range [0, %d]", bs, ctx->cfg.max_batch);
+  if (num_tokens < 0 || num_tokens > ctx->cfg.max_q_tokens)
+    return fail(VA_ERR_INVALID, "num_tokens %lld out of range [0, %lld]",
+                (long long)num_tokens, (long long)ctx->cfg.max_q_tokens);
+  if (num_slots < 1) return fail(VA_ERR_INVALID, "num_slots must be >= 1");
+  if (num_kv_indices < 0 || mask_len < 0)
+    return fail(VA_ERR_INVALID, "num_kv_indices and mask_len must be >= 0");
+  if (!isfinite(sm_scale)) return fail(VA_ERR_INVALID, "sm_scale must be finite");
+  if (num_tokens == 0) return ok();
+  if (!out) return fail(VA_ERR_NULL, "out is NULL");
+  if (bs > 0) {
+    if (!q || !kv_buffer || !kv_indptr || !qo_indptr || !mask_indptr)
+      return fail(VA_ERR_NULL, "a required input pointer is NULL");
+    if (num_kv_indices > 0 && !kv_indices) return fail(VA_ERR_NULL, "kv_indices is NULL");
+    if (mask_len > 0 && !custom_mask) return fail(VA_ERR_NULL, "custom_mask is NULL");
+  }
+  va::RunArgs a;
+  a.q = q;
+  a.kv = kv_buffer;
+  a.num_slots = num_slots;
+  a.kv_indices = kv_indices;
+  a.num_kv_indices = num_kv_indices;
+  a.kv_indptr = kv_indptr;
+  a.qo_indptr = qo_indptr;
+  a.mask = custom_mask;
+  a.mask_len = mask_len;
+  a.mask_indptr = mask_indptr;
+  a.bs = bs;
+  a.num_tokens = num_tokens;
+  a.H = ctx->cfg.num_heads;
+  a.max_q_per_req = ctx->cfg.max_q_per_req;
+  a.scale = sm_scale;
+  a.out = out;
+  a.out_lse = out_lse;
+  a.out_argmax = out_argmax;
+  a.out_bf16 = ctx->cfg.out_dtype == VA_BF16;
+  a.want_argmax = out_argmax != nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (ctx->ev[0] && (e = hipEventRecord(ctx->ev[0], st)) != hipSuccess)
+    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  if (bs > 0) {
+    if (ctx->kernel == VA_KERNEL_SIMPLE)
+      e = va::launch_simple_partial(a, ctx->ws, ctx->cfg.in_dtype == VA_FP32, st);
+    else
+      e = va::launch_mfma_partial(a, ctx->ws, ctx->rows_per_block, st);
+    if (e != hipSuccess)
+      return fail(VA_ERR_HIP, "partial kernel launch failed: %s", hipGetErrorString(e));
+  }
+  if (ctx->ev[1] && (e = hipEventRecord(ctx->ev[1], st)) != hipSuccess)
+    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  e = va::launch_combine(a, ctx->ws, st);
+  if (e != hipSuccess)
+    return fail(VA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
+  if (ctx->ev[2] && (e = hipEventRecord(ctx->ev[2], st)) != hipSuccess)
+    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+va_status verify_attn_read_device_status(verify_attn_ctx *ctx, void *stream, uint32_t *flags) {
+  if (!ctx || !flags) return fail(VA_ERR_NULL, "ctx or flags is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = hipMemcpy(&v, ctx->ws.status, sizeof v, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(ctx->ws.status, 0, sizeof v);
+  if (e != hipSuccess) return fail(VA_ERR_HIP, "status read failed: %s", hipGetErrorString(e));
+  *flags = v;
+  return ok();
+}
+
+va_status verify_attn_set_profiling_events(verify_attn_ctx *ctx, void *before, void *between,
+                                           void *after) {
+  if (!ctx) return fail(VA_ERR_NULL, "ctx is NULL");
+  const bool all = before && between && after;
+  const bool none = !before && !between && !after;
+  if (!all && !none) return fail(VA_ERR_INVALID, "pass three events or none");
+  ctx->ev[0] = static_cast<hipEvent_t>(before);
+  ctx->ev[1] = static_cast<hipEvent_t>(between);
+  ctx->ev[2] = static_cast<hipEvent_t>(after);
+  return ok();
+}
+
+va_status verify_attn_get_info(const verify_attn_ctx *ctx, verify_attn_info *info) {
+  if (!ctx || !info) return fail(VA_ERR_NULL, "ctx or info is NULL");
+  info->kernel = ctx->kernel;
+  info->num_splits = ctx->splits;
+  info->rows_per_block = ctx->rows_per_block;
+  info->row_tiles_per_req = ctx->row_tiles_per_req;
+  info->workspace_bytes = ctx->ws_bytes;
+  return ok();
+}
+
+void verify_attn_destroy(verify_attn_ctx *ctx) {
+  if (!ctx) return;
+  if (ctx->ws_owned && ctx->ws_base) (void)hipFree(ctx->ws_base);
+  delete ctx;
+}
+
+const char *verify_attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

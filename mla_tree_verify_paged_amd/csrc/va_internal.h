@@ -1,0 +1,112 @@
+// va_internal.h - declarations shared by the library's translation units (not installed).
+//
+// Workspace layout (all offsets 256-byte aligned), for S splits and R = max_q_tokens * H rows:
+//   status   uint32 [64]            sticky VA_DEV_* bits in word 0
+//   part_o   float  [S][R][512]     per-split normalised output O_s
+//   part_lse float  [S][R]          per-split log-sum-exp (natural log); -inf for an empty split
+//   part_max float  [S][R]          per-split max score (natural-log units)
+//   part_arg int32  [S][R]          per-split argmax key position (-1 when empty)
+// A partial row (s, t*H+h) is written by the partial kernel for every split s of the request
+// that owns token t, including empty splits, whenever the request's segment is valid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace va {
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kDim = kLatent + kRope;  // 576
+constexpr int kMaxSplits = 256;
+
+struct Workspace {
+  uint32_t *status;
+  float *part_o;
+  float *part_lse;
+  float *part_max;
+  int32_t *part_arg;
+  int64_t rows_cap;  // R
+  int32_t splits;    // S
+};
+
+// Arguments of one verify step, as the kernels see them.
+struct RunArgs {
+  const void *q;
+  const void *kv;
+  int64_t num_slots;
+  const int64_t *kv_indices;
+  int64_t num_kv_indices;
+  const int32_t *kv_indptr;
+  const int64_t *qo_indptr;
+  const uint8_t *mask;
+  int64_t mask_len;
+  const int64_t *mask_indptr;
+  int32_t bs;
+  int64_t num_tokens;
+  int32_t H;
+  int32_t max_q_per_req;
+  float scale;  // natural-log units
+  void *out;
+  float *out_lse;
+  int32_t *out_argmax;
+  int32_t out_bf16;
+  int32_t want_argmax;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte offsets of the workspace regions for S splits and R rows; returns the total size.
+inline size_t workspace_layout(int32_t S, int64_t R, size_t off[5]) {
+  size_t o = 0;
+  off[0] = o; o = align256(o + 64 * sizeof(uint32_t));
+  off[1] = o; o = align256(o + size_t(S) * size_t(R) * kLatent * sizeof(float));
+  off[2] = o; o = align256(o + size_t(S) * size_t(R) * sizeof(float));
+  off[3] = o; o = align256(o + size_t(S) * size_t(R) * sizeof(float));
+  off[4] = o; o = align256(o + size_t(S) * size_t(R) * sizeof(int32_t));
+  return o;
+}
+
+// Per-request segment validation shared by every kernel (device side). Sets *T, *L, bases,
+// and returns a VA_DEV_* bit (0 when the segment is usable).
+struct Segment {
+  int64_t q0;     // first token
+  int32_t T;      // tree tokens
+  int32_t L;      // keys
+  int32_t P;      // prefix keys
+  int64_t kv0;    // first kv_indices entry
+  int64_t m0;     // first mask byte
+};
+
+__device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segment &s) {
+  const int64_t q0 = a.qo_indptr[r], q1 = a.qo_indptr[r + 1];
+  const int64_t k0 = a.kv_indptr[r], k1 = a.kv_indptr[r + 1];
+  const int64_t m0 = a.mask_indptr[r];
+  s.q0 = q0;
+  s.kv0 = k0;
+  s.m0 = m0;
+  const int64_t T = q1 - q0, L = k1 - k0;
+  s.T = 0; s.L = 0; s.P = 0;
+  if (T < 0 || L < 0 || q0 < 0 || q1 > a.num_tokens || k0 < 0 || k1 > a.num_kv_indices ||
+      L < T || m0 < 0 || (T > 0 && m0 + T * L > a.mask_len))
+    return 2u;  // VA_DEV_SEGMENT
+  if (T > a.max_q_per_req) return 4u;  // VA_DEV_Q_PER_REQ
+  s.T = int32_t(T);
+  s.L = int32_t(L);
+  s.P = int32_t(L - T);
+  return 0u;
+}
+
+// Launchers (each defined next to its kernels).
+hipError_t launch_simple_partial(const RunArgs &a, const Workspace &ws, int in_fp32,
+                                 hipStream_t st);
+hipError_t launch_mfma_partial(const RunArgs &a, const Workspace &ws, int rows_per_block,
+                               hipStream_t st);
+hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st);
+
+// Rows per workgroup of each partial kernel (fixes the grid).
+constexpr int kSimpleHeadsPerBlock = 4;
+constexpr int kMfmaRowsPerBlock = 128;
+
+}  // namespace va

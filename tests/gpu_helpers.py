@@ -1,0 +1,98 @@
+"""Shared helpers for the GPU tests: run a workload through the C ABI, run the oracle on the
+same inputs, compare."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+import oracle
+import workloads as wl
+
+OUT_TOL = 1e-2      # max-abs on out, bf16 inputs with fp32 accumulation (and fp32 inputs)
+LSE_RTOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w, kernel="auto", num_splits=0, out_dtype="fp32", want_lse=True, want_argmax=True,
+            max_batch=None, max_q_per_req=None, max_q_tokens=None, dev=None, va=None):
+    """Runs workload `w` through the C ABI. Returns (out f64 [rows,512], lse, argmax, status)."""
+    import torch
+    from mla_tree_verify_paged_amd import VerifyAttn
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+    if dev is None:
+        dev = to_device(w)
+    if va is None:
+        va = VerifyAttn(w.num_heads, in_dtype=w.in_dtype, out_dtype=out_dtype,
+                        max_batch=max_batch or max(1, w.bs),
+                        max_q_per_req=max_q_per_req or max(1, w.max_q_per_req),
+                        max_q_tokens=max_q_tokens or max(1, w.num_tokens),
+                        num_splits=num_splits, kernel=kernel)
+    n = w.num_tokens
+    odt = torch.float32 if out_dtype == "fp32" else torch.bfloat16
+    out = torch.full((n, w.num_heads, 512), float("nan"), dtype=odt, device="cuda")
+    lse = torch.full((n, w.num_heads), float("nan"), dtype=torch.float32, device="cuda") \
+        if want_lse else None
+    am = torch.full((n, w.num_heads), -7, dtype=torch.int32, device="cuda") \
+        if want_argmax else None
+    va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"], dev["qo_indptr"],
+           dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, am, bs=w.bs,
+           num_tokens=n)
+    torch.cuda.synchronize()
+    status = va.read_device_status()
+    o = out.float().cpu().numpy().astype(np.float64).reshape(n * w.num_heads, 512)
+    l = lse.cpu().numpy().astype(np.float64).ravel() if want_lse else None
+    a = am.cpu().numpy().astype(np.int64).ravel() if want_argmax else None
+    return o, l, a, status
+
+
+def sample_rows(w, n, seed=0, must=()):
+    rows_total = w.num_tokens * w.num_heads
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(rows_total, size=min(n, rows_total), replace=False)
+    rows = np.unique(np.concatenate([rows, np.asarray(must, dtype=np.int64)]))
+    return rows.astype(np.int64)
+
+
+def run_oracle(w, rows=None, pool=None):
+    t0 = time.time()
+    res = oracle.run_workload(w, rows=rows, pool=pool)
+    say(f"  oracle {w.name}: {0 if rows is None else len(rows)} rows in {time.time() - t0:.1f}s")
+    return res
+
+
+def compare(w, gpu, ref, rows=None, exact_argmax=False, tol=OUT_TOL):
+    o, l, a, status = gpu
+    ro, rl, ra = ref
+    if rows is not None:
+        o = o[rows]
+        l = None if l is None else l[rows]
+        a = None if a is None else a[rows]
+    err = float(np.max(np.abs(o - ro))) if o.size else 0.0
+    say(f"  {w.name}: max|out-ref| = {err:.3e} over {o.shape[0]} rows, status={status}")
+    assert status == 0, f"device status {status}"
+    assert np.all(np.isfinite(o)), "non-finite output"
+    assert err <= tol, f"max abs err {err} > {tol}"
+    if l is not None:
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(l), fin)
+        rel = np.abs(l[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin]))
+        assert rel.size == 0 or rel.max() <= LSE_RTOL, f"lse rel err {rel.max()}"
+    if a is not None and exact_argmax:
+        assert np.array_equal(a, ra), "argmax differs"
+    return err
+
+
+def stress_depth8_rows(w):
+    """Flat rows (t*H + h, head 0) of every depth-8 tree node of the stress workload."""
+    rows = []
+    for r in range(w.bs):
+        d = wl.tree_depths(w.parents[r])
+        for i in np.nonzero(d == d.max())[0]:
+            rows.append((int(w.qo_indptr[r]) + int(i)) * w.num_heads)
+    return rows

@@ -1,0 +1,86 @@
+"""Capture safety: verify_attn_run recorded into a HIP graph and replayed after the contents
+of the static buffers change (new queries, new KV rows, a different prefix length and tree)
+gives the eager result bit for bit and matches the oracle on every replay."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.conftest import gpu_available
+from tests.gpu_helpers import compare, run_oracle, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+KERNELS = ["simple"]
+
+
+def make(seed, p, t):
+    return wl.build_workload(f"g{seed}", np.random.default_rng(seed), 64, [p], [t], 65536)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_graph_replay_with_new_buffer_contents(kernel):
+    from mla_tree_verify_paged_amd import VerifyAttn
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+    max_t, max_l = 16, 4000
+    va = VerifyAttn(64, max_batch=1, max_q_per_req=max_t, max_q_tokens=max_t, kernel=kernel)
+    # static buffers sized for the largest step
+    q = torch.zeros((max_t, 64, 576), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((65536, 576), dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros(max_l, dtype=torch.int64, device="cuda")
+    kv_indptr = torch.zeros(2, dtype=torch.int32, device="cuda")
+    qo_indptr = torch.zeros(2, dtype=torch.int64, device="cuda")
+    mask = torch.zeros(max_t * max_l, dtype=torch.uint8, device="cuda")
+    mask_indptr = torch.zeros(2, dtype=torch.int64, device="cuda")
+    out = torch.zeros((max_t, 64, 512), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((max_t, 64), dtype=torch.float32, device="cuda")
+
+    def load(w):
+        d = to_device(w)
+        n = w.num_tokens
+        q.zero_()
+        q[:n].copy_(d["q"])
+        pool.copy_(d["kv_buffer"])
+        idx[:d["kv_indices"].numel()].copy_(d["kv_indices"])
+        kv_indptr.copy_(d["kv_indptr"])
+        qo_indptr.copy_(d["qo_indptr"])
+        mask[:d["custom_mask"].numel()].copy_(d["custom_mask"])
+        mask_indptr.copy_(d["mask_indptr"])
+
+    def step():
+        va.run(q, pool, idx, kv_indptr, qo_indptr, mask, mask_indptr, wl.DEFAULT_SCALE, out,
+               lse, None, bs=1, num_tokens=max_t)
+
+    # the graph is recorded once with num_tokens = max_t; steps with fewer tokens leave the
+    # extra rows empty (qo_indptr covers fewer tokens), which the C ABI reports in its status
+    w0 = make(100, 3000, 16)
+    load(w0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    for seed, p, t in ((101, 3000, 16), (102, 1200, 16), (103, 3984, 16), (104, 2500, 16)):
+        w = make(seed, p, t)
+        load(w)
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64).reshape(-1, 512)
+        got_lse = lse.cpu().numpy().astype(np.float64).ravel()
+        # eager on the same buffers
+        step()
+        torch.cuda.synchronize()
+        eager = out.cpu().numpy().astype(np.float64).reshape(-1, 512)
+        assert np.array_equal(got, eager), "replay differs from eager"
+        st = va.read_device_status()
+        say(f"replay seed={seed} P={p}")
+        ref = run_oracle(w)
+        compare(w, (got, got_lse, None, st), ref)

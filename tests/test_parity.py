@@ -1,0 +1,161 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same seeded inputs.
+
+Bar: max |out - oracle| <= 1e-2 (fp32 out), lse within 1e-4 relative, the argmax equal on
+every row of the tiny fp32 workload, device status clean."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.conftest import gpu_available
+from tests.gpu_helpers import (compare, run_gpu, run_oracle, sample_rows, say,
+                               stress_depth8_rows)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+BF16_KERNELS = ["simple"]
+
+
+def test_tiny_fp32_exact_argmax():
+    w = wl.tiny()
+    say("tiny fp32, simple kernel")
+    ref = run_oracle(w)
+    for splits in (0, 1, 3, 64):
+        gpu = run_gpu(w, kernel="simple", num_splits=splits)
+        err = compare(w, gpu, ref, exact_argmax=True)
+        assert err <= 1e-4  # fp32 inputs and arithmetic
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_short(kernel):
+    w = wl.short()
+    say(f"short, {kernel}")
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_long_full(kernel):
+    w = wl.long()
+    say(f"long, {kernel}")
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_segmented_sampled(kernel):
+    w = wl.segmented()
+    rows = sample_rows(w, 384, seed=1)
+    say(f"segmented, {kernel}, {len(rows)} sampled rows")
+    ref = run_oracle(w, rows=rows)
+    compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_stress_sampled(kernel):
+    w = wl.stress()
+    rows = sample_rows(w, 96, seed=2, must=stress_depth8_rows(w))
+    say(f"stress, {kernel}, {len(rows)} sampled rows")
+    ref = run_oracle(w, rows=rows)
+    compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
+
+
+# ----------------------------------------------------------------------------- seeded fuzz
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+@pytest.mark.parametrize("seed", range(6))
+def test_fuzz_small_shapes(kernel, seed):
+    rng = np.random.default_rng(500 + seed)
+    bs = int(rng.integers(1, 5))
+    h = int(rng.choice([1, 3, 8, 64]))
+    t = rng.integers(1, 34, bs)
+    p = rng.integers(0, 3001, bs)
+    w = wl.build_workload(f"fuzz{seed}", rng, h, p, t, int((p + t).sum()) * 2 + 7)
+    splits = int(rng.choice([0, 1, 5, 17]))
+    say(f"fuzz seed={seed} {kernel}: bs={bs} H={h} T={t.tolist()} P={p.tolist()} S={splits}")
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel, num_splits=splits), ref)
+
+
+# ----------------------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_zero_prefix_and_single_token(kernel):
+    rng = np.random.default_rng(7)
+    w = wl.build_workload("p0", rng, 8, [0, 0, 5], [1, 7, 1], 64)
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_more_splits_than_keys(kernel):
+    rng = np.random.default_rng(8)
+    w = wl.build_workload("split", rng, 16, [3, 40], [2, 5], 128)
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel, num_splits=64), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_fully_masked_rows_are_empty(kernel):
+    rng = np.random.default_rng(9)
+    w = wl.build_workload("masked", rng, 4, [0], [6], 32)
+    m = w.custom_mask.reshape(6, 6)
+    m[2, :] = 0
+    m[4, :] = 0
+    ref = run_oracle(w)
+    o, l, a, st = run_gpu(w, kernel=kernel)
+    for tok in (2, 4):
+        rows = slice(tok * 4, tok * 4 + 4)
+        assert np.all(o[rows] == 0) and np.all(l[rows] == -np.inf) and np.all(a[rows] == -1)
+    compare(w, (o, l, a, st), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_request_without_tree_tokens(kernel):
+    rng = np.random.default_rng(10)
+    w = wl.build_workload("t0", rng, 8, [50, 30, 70], [3, 0, 4], 256)
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_bf16_output(kernel):
+    w = wl.short()
+    ref = run_oracle(w)
+    o, l, a, st = run_gpu(w, kernel=kernel, out_dtype="bf16")
+    err = np.abs(o - ref[0])
+    bound = 1e-2 + np.abs(ref[0]) * 2.0 ** -8
+    assert np.all(err <= bound), float((err - bound).max())
+    assert st == 0
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_optional_outputs_may_be_null(kernel):
+    w = wl.build_workload("null", np.random.default_rng(11), 8, [100], [5], 256)
+    ref = run_oracle(w)
+    o, _, _, st = run_gpu(w, kernel=kernel, want_lse=False, want_argmax=False)
+    compare(w, (o, None, None, st), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_oversized_bounds(kernel):
+    """A context sized for more requests and tokens than the call uses."""
+    rng = np.random.default_rng(12)
+    w = wl.build_workload("big", rng, 64, [700, 20], [9, 16], 2048)
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel, max_batch=5, max_q_per_req=40, max_q_tokens=200), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_bitwise_deterministic(kernel):
+    w = wl.build_workload("det", np.random.default_rng(13), 64, [1500], [16], 4096)
+    a = run_gpu(w, kernel=kernel)
+    b = run_gpu(w, kernel=kernel)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.skipif("mfma" not in BF16_KERNELS, reason="MFMA kernel not built yet")
+def test_mfma_matches_simple_closely():
+    """Both kernels agree far inside the oracle tolerance."""
+    w = wl.build_workload("xk", np.random.default_rng(14), 64, [2000, 900], [16, 8], 8192)
+    a = run_gpu(w, kernel="simple")
+    b = run_gpu(w, kernel="mfma")
+    assert np.max(np.abs(a[0] - b[0])) <= 5e-3

@@ -1,0 +1,78 @@
+"""Bad device-side data never faults: the offending key or request is ignored, the rows it
+touches are written as documented, and the sticky status word reports it."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from mla_tree_verify_paged_amd import binding as B
+from tests.conftest import gpu_available
+from tests.gpu_helpers import compare, run_gpu, run_oracle
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+KERNELS = ["simple"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_out_of_range_slot_is_ignored_and_flagged(kernel):
+    w = wl.build_workload("slot", np.random.default_rng(20), 8, [40], [4], 128)
+    p = 40
+    # reference: tree key 3 hidden from every query
+    ref_w = wl.build_workload("slot", np.random.default_rng(20), 8, [40], [4], 128)
+    ref_w.custom_mask.reshape(4, 44)[:, p + 3] = 0
+    ref = run_oracle(ref_w)
+    w.kv_indices[p + 3] = w.num_slots + 5
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+    dev = to_device(ref_w)
+    dev["kv_indices"][p + 3] = w.num_slots + 5
+    o, l, a, st = run_gpu(w, kernel=kernel, dev=dev)
+    assert st & B.VA_DEV_SLOT_RANGE
+    compare(w, (o, l, a, 0), ref)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_too_many_tree_tokens_for_the_context(kernel):
+    w = wl.build_workload("tq", np.random.default_rng(21), 8, [30, 30], [3, 9], 128)
+    o, l, a, st = run_gpu(w, kernel=kernel, max_q_per_req=4, max_q_tokens=12)
+    assert st & B.VA_DEV_Q_PER_REQ
+    ref = run_oracle(w)
+    first = 3 * 8
+    compare(w, (o[:first], l[:first], a[:first], 0), (ref[0][:first], ref[1][:first],
+                                                       ref[2][:first]))
+    assert np.all(o[first:] == 0) and np.all(l[first:] == -np.inf) and np.all(a[first:] == -1)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_prefix_shorter_than_tree_is_flagged(kernel):
+    w = wl.build_workload("seg", np.random.default_rng(22), 4, [10, 20], [4, 4], 128)
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+    dev = to_device(w)
+    dev["kv_indptr"][1] = 2          # request 0: L=2 < T=4; request 1: L=32
+    o, l, a, st = run_gpu(w, kernel=kernel, dev=dev)
+    assert st & B.VA_DEV_SEGMENT
+    assert np.all(o[:16] == 0) and np.all(l[:16] == -np.inf)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_tokens_not_covered_by_qo_indptr(kernel):
+    """num_tokens = 7 but qo_indptr covers 5 tokens: rows of tokens 5 and 6 are empty."""
+    import torch
+    from mla_tree_verify_paged_amd import VerifyAttn
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+    w = wl.build_workload("tok", np.random.default_rng(23), 4, [16], [5], 64)
+    dev = to_device(w)
+    q = torch.cat([dev["q"], dev["q"][:2]])
+    va = VerifyAttn(4, max_batch=1, max_q_per_req=5, max_q_tokens=7, kernel=kernel)
+    out = torch.full((7, 4, 512), float("nan"), device="cuda")
+    lse = torch.zeros((7, 4), device="cuda")
+    va.run(q, dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"], dev["qo_indptr"],
+           dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, None, bs=1, num_tokens=7)
+    st = va.read_device_status()
+    assert st & B.VA_DEV_TOKENS
+    o = out.cpu().numpy()
+    assert np.all(o[5:] == 0) and np.all(np.isfinite(o))
+    assert np.all(lse.cpu().numpy()[5:] == -np.inf)
+    ref = run_oracle(w)
+    compare(w, (o[:5].reshape(-1, 512).astype(np.float64), lse.cpu().numpy()[:5].ravel(), None,
+                0), ref)
