@@ -12,7 +12,7 @@ from tests.gpu_helpers import compare, run_oracle, say
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-KERNELS = ["simple"]
+KERNELS = ["simple", "mfma"]
 
 
 def make(seed, p, t):

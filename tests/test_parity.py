@@ -13,7 +13,7 @@ from tests.gpu_helpers import (compare, run_gpu, run_oracle, sample_rows, say,
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-BF16_KERNELS = ["simple"]
+BF16_KERNELS = ["simple", "mfma"]
 
 
 def test_tiny_fp32_exact_argmax():

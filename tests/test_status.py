@@ -11,7 +11,7 @@ from tests.gpu_helpers import compare, run_gpu, run_oracle
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-KERNELS = ["simple"]
+KERNELS = ["simple", "mfma"]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
