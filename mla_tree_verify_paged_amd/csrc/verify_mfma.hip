@@ -19,7 +19,7 @@
 //  * S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16: A = key rows from LDS, B = the wave's 32
 //    query rows held in registers. The accumulator gives each lane one row and 16 keys, so a
 //    softmax row reduction is one cross-lane swap;
-//  * P is rounded to fp16 and O^T += V^T P^T runs on v_mfma_f32_32x32x16_f16. V is the first
+//  * P is rounded (to nearest even) to fp16 and O^T += V^T P^T runs on v_mfma_f32_32x32x16_f16. V is the first
 //    512 dims of the same rows, converted to fp16 by the thread that loaded each unit while
 //    the previous tile's products run, and read as V^T fragments with ds_read_b64_tr_b16.
 //    The P fragment is the S accumulator itself: key slots are permuted the same way in both
@@ -41,6 +41,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__fp16)))) __fp16 fp16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
 
 constexpr int kThreads = 256;
@@ -354,12 +356,15 @@ __device__ __forceinline__ void tile_step(const Ctx &c0, int t, int ntiles, Wave
   for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(sacc[8 * ch + e] - msafe);
-      const float p1 = __builtin_amdgcn_exp2f(sacc[8 * ch + e + 1] - msafe);
-      const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
-      st.lsum += float(h[0]) + float(h[1]);
-      pf[ch][e] = (_Float16)h[0];
-      pf[ch][e + 1] = (_Float16)h[1];
+      f32x2 p;
+      p.x = __builtin_amdgcn_exp2f(sacc[8 * ch + e] - msafe);
+      p.y = __builtin_amdgcn_exp2f(sacc[8 * ch + e + 1] - msafe);
+      // round to nearest even (v_cvt_pk_f16_f32): unbiased, so the denominator summed from
+      // the rounded values does not drift low
+      const f16x2v h = __builtin_convertvector(p, f16x2v);
+      st.lsum += float(h.x) + float(h.y);
+      pf[ch][e] = h.x;
+      pf[ch][e + 1] = h.y;
     }
   }
 

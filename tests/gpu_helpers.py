@@ -11,7 +11,11 @@ import oracle
 import workloads as wl
 
 OUT_TOL = 1e-2      # max-abs on out, bf16 inputs with fp32 accumulation (and fp32 inputs)
-LSE_RTOL = 1e-4
+# lse: the MFMA path rounds each softmax weight to fp16 (relative error <= 2^-11) and sums the
+# rounded weights, so the denominator, hence lse, may move by up to 2^-11 in natural-log units;
+# twice that plus fp32 score rounding is the bound.
+LSE_ATOL = 2.0 ** -10
+LSE_RTOL = 1e-5
 
 
 def say(*a):
@@ -81,8 +85,8 @@ def compare(w, gpu, ref, rows=None, exact_argmax=False, tol=OUT_TOL):
     if l is not None:
         fin = np.isfinite(rl)
         assert np.array_equal(np.isfinite(l), fin)
-        rel = np.abs(l[fin] - rl[fin]) / np.maximum(1.0, np.abs(rl[fin]))
-        assert rel.size == 0 or rel.max() <= LSE_RTOL, f"lse rel err {rel.max()}"
+        excess = np.abs(l[fin] - rl[fin]) - (LSE_ATOL + LSE_RTOL * np.abs(rl[fin]))
+        assert excess.size == 0 or excess.max() <= 0, f"lse error exceeds bound by {excess.max()}"
     if a is not None and exact_argmax:
         assert np.array_equal(a, ra), "argmax differs"
     return err
