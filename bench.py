@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy (for scaling "
+                         "hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -211,6 +214,14 @@ def main():
     cold = np.array(cold)
     del flush
     log(f"graph warm {graph_us:.2f} us/step; cold median {np.median(cold):.2f} us")
+
+    if args.copy_calibration:
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     by, fl = algorithmic_work(w)
     part_s = part_ms.mean() * 1e-3

@@ -82,7 +82,8 @@ enum { VA_KERNEL_AUTO = 0, VA_KERNEL_SIMPLE = 1, VA_KERNEL_MFMA = 2 };
 /* sticky device status bits (verify_attn_read_device_status) */
 enum {
   VA_DEV_SLOT_RANGE = 1u,  /* a kv_indices entry outside [0, num_slots): key ignored        */
-  VA_DEV_SEGMENT = 2u,     /* L_r < T_r, or offsets outside kv_indices / mask / q: rows empty */
+  VA_DEV_SEGMENT = 2u,     /* L_r < T_r, offsets outside kv_indices / mask / q, or a request
+                              whose mask segment T_r*L_r reaches 2^31 bytes: rows empty */
   VA_DEV_Q_PER_REQ = 4u,   /* T_r > max_q_per_req: the request's rows written empty         */
   VA_DEV_TOKENS = 8u       /* qo_indptr[bs] != num_tokens: uncovered rows written empty     */
 };
@@ -130,8 +131,8 @@ va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **ou
  *   out          [num_tokens, H, 512] out_dtype.
  *   out_lse      nullable float [num_tokens, H].
  *   out_argmax   nullable int32 [num_tokens, H].
- * Host-checked: pointers, 0 <= bs <= max_batch, 0 <= num_tokens <= max_q_tokens, finite
- * sm_scale, num_slots >= 1. Returns VA_ERR_HIP if a launch fails.
+ * Host-checked: pointers, 0 <= bs <= max_batch, 0 <= num_tokens <= max_q_tokens,
+ * 0 < sm_scale < inf, num_slots >= 1. Returns VA_ERR_HIP if a launch fails.
  */
 va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_buffer,
                           int64_t num_slots, const int64_t *kv_indices, int64_t num_kv_indices,

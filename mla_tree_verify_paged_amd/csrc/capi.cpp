@@ -200,7 +200,8 @@ va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_bu
   if (num_slots < 1) return fail(VA_ERR_INVALID, "num_slots must be >= 1");
   if (num_kv_indices < 0 || mask_len < 0)
     return fail(VA_ERR_INVALID, "num_kv_indices and mask_len must be >= 0");
-  if (!isfinite(sm_scale)) return fail(VA_ERR_INVALID, "sm_scale must be finite");
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return fail(VA_ERR_INVALID, "sm_scale must be positive and finite");
   if (num_tokens == 0) return ok();
   if (!out) return fail(VA_ERR_NULL, "out is NULL");
   if (bs > 0) {

@@ -89,8 +89,9 @@ __device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segmen
   const int64_t T = q1 - q0, L = k1 - k0;
   s.T = 0; s.L = 0; s.P = 0;
   if (T < 0 || L < 0 || q0 < 0 || q1 > a.num_tokens || k0 < 0 || k1 > a.num_kv_indices ||
-      L < T || m0 < 0 || (T > 0 && m0 + T * L > a.mask_len))
-    return 2u;  // VA_DEV_SEGMENT
+      L < T || L > INT32_MAX || m0 < 0 || (T > 0 && m0 + T * L > a.mask_len) ||
+      T * L > INT32_MAX)
+    return 2u;  // VA_DEV_SEGMENT (a request's mask segment must stay under 2 GiB)
   if (T > a.max_q_per_req) return 4u;  // VA_DEV_Q_PER_REQ
   s.T = int32_t(T);
   s.L = int32_t(L);

@@ -8,7 +8,9 @@
 // and the argmax is the argmax of the split holding the largest max score (lowest split,
 // hence lowest key position, on ties).
 //
-// One wavefront per row; lane l owns output dims [8l, 8l+8). The combine also owns output
+// One wavefront per row. The per-split scalars are read lane-parallel (lane s holds split s);
+// the 2 KB partial rows of the splits with nonzero weight are then streamed with up to eight
+// splits in flight, lane l owning output dims [8l, 8l+8). The combine also owns output
 // validation: a row whose token belongs to no valid request is written empty (out 0,
 // lse -inf, argmax -1) and the matching status bit is set, so every output element is
 // defined whatever the device-side tables hold.
@@ -21,6 +23,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kThreads / 64;
+constexpr int kBatch = 8;  // splits whose partial rows are in flight at once
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -91,11 +94,18 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   }
 
   const int S = ws.splits;
-  // max over splits of lse and of the max score
+  const float *plse = ws.part_lse + row;
+  const float *pmax = ws.part_max + row;
+  const int64_t stride = ws.rows_cap;
+
+  // per-split scalars, lane-parallel
   float M = -INFINITY, best = -INFINITY;
-  for (int s = lane; s < S; s += 64) {
-    M = fmaxf(M, ws.part_lse[int64_t(s) * ws.rows_cap + row]);
-    best = fmaxf(best, ws.part_max[int64_t(s) * ws.rows_cap + row]);
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    if (s < S) {
+      M = fmaxf(M, plse[s * stride]);
+      best = fmaxf(best, pmax[s * stride]);
+    }
   }
   M = wave_max(M);
   best = wave_max(best);
@@ -103,19 +113,52 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   float W = 0.f;
   int arg = -1;
   if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const int64_t prow = int64_t(s) * ws.rows_cap + row;
-      const float ls = ws.part_lse[prow];
-      if (ls == -INFINITY) continue;
-      const float w = expf(ls - M);
-      W += w;
-      const float4 *src = reinterpret_cast<const float4 *>(ws.part_o + prow * kLatent);
-      const float4 x0 = src[2 * lane], x1 = src[2 * lane + 1];
-      v[0] = fmaf(w, x0.x, v[0]); v[1] = fmaf(w, x0.y, v[1]);
-      v[2] = fmaf(w, x0.z, v[2]); v[3] = fmaf(w, x0.w, v[3]);
-      v[4] = fmaf(w, x1.x, v[4]); v[5] = fmaf(w, x1.y, v[5]);
-      v[6] = fmaf(w, x1.z, v[6]); v[7] = fmaf(w, x1.w, v[7]);
-      if (arg < 0 && ws.part_max[prow] == best) arg = ws.part_arg[prow];
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int s = s0 + lane;
+      const float ls = s < S ? plse[s * stride] : -INFINITY;
+      const float w = ls == -INFINITY ? 0.f : expf(ls - M);
+      W += wave_sum(w);
+      if (arg < 0) {
+        const uint64_t hit = __ballot(s < S && pmax[s * stride] == best);
+        if (hit) arg = ws.part_arg[(s0 + __builtin_ctzll(hit)) * stride + row];
+      }
+      uint64_t live = __ballot(w != 0.f);
+      while (live) {
+        // up to kBatch splits with nonzero weight: issue their loads, then accumulate
+        int idx[kBatch];
+        float wt[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          idx[k] = -1;
+          wt[k] = 0.f;
+          if (live) {
+            const int j = __builtin_ctzll(live);
+            live &= live - 1;
+            idx[k] = s0 + j;
+            wt[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+          }
+        }
+        float4 x0[kBatch], x1[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          if (idx[k] >= 0) {
+            const float4 *src = reinterpret_cast<const float4 *>(
+                ws.part_o + (int64_t(idx[k]) * stride + row) * kLatent);
+            x0[k] = src[2 * lane];
+            x1[k] = src[2 * lane + 1];
+          } else {
+            x0[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            x1[k] = x0[k];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          v[0] = fmaf(wt[k], x0[k].x, v[0]); v[1] = fmaf(wt[k], x0[k].y, v[1]);
+          v[2] = fmaf(wt[k], x0[k].z, v[2]); v[3] = fmaf(wt[k], x0[k].w, v[3]);
+          v[4] = fmaf(wt[k], x1[k].x, v[4]); v[5] = fmaf(wt[k], x1[k].y, v[5]);
+          v[6] = fmaf(wt[k], x1[k].z, v[6]); v[7] = fmaf(wt[k], x1[k].w, v[7]);
+        }
+      }
     }
     const float inv = 1.f / W;
 #pragma unroll

@@ -62,6 +62,8 @@ constexpr int kDBlocks = kLatent / 32;      // 16 output dim blocks of 32
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;            // lazy-rescale threshold (log2 units)
+constexpr int kKPrefetch = 7;               // K-fragment LDS reads kept in flight per wave
+constexpr int kVPrefetch = 8;               // V-fragment (pairs of transposed) reads in flight
 
 static_assert(kRowsPerWave == 8, "one rope load instruction covers 8 rows");
 
@@ -89,6 +91,17 @@ __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
 
 __device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
 __device__ __forceinline__ int swap_halves(int v) { return __shfl_xor(v, 32, 64); }
+
+// The value lane l ^ 32 holds (v_permlane32_swap, no LDS round trip).
+__device__ __forceinline__ int other_half(int v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  // r[0]: lanes 0-31 keep v[lane], lanes 32-63 get v[lane-32]; r[1]: lanes 0-31 get
+  // v[lane+32], lanes 32-63 keep v[lane]
+  return (__lane_id() < 32) ? int(r[1]) : int(r[0]);
+}
+__device__ __forceinline__ float other_half(float v) {
+  return __int_as_float(other_half(__float_as_int(v)));
+}
 
 // Register-class hint: the 256 output accumulators live in AGPRs for the whole kernel.
 // (Empty inline assembly with a register-class constraint; it emits no instruction.)
@@ -242,12 +255,13 @@ struct RowState {
   int best_j;   // argmax key position
 };
 
-// One key tile t in buffer B: QK^T, mask, online softmax, PV. Meanwhile tile t+1 is loaded
-// into buffer B^1 and converted, and the slots of tile t+2 are fetched.
+// One key tile t in buffer B: QK^T, mask, online softmax, PV. Tile t+1 is loaded into buffer
+// B^1 meanwhile (issued first, waited for and converted last), and the slots of tile t+2 are
+// fetched.
 template <int B, bool kArgmax>
 __device__ __forceinline__ void tile_step(const Ctx &c0, int t, int ntiles, WaveSlots &slots,
                                           const bf16x8 *qf, f32x16 *o, RowState &st, float c2,
-                                          bool row_ok, const uint8_t *mrow) {
+                                          bool row_ok, const uint8_t *mseg, uint32_t moff) {
   constexpr int NB = B ^ 1;
   Ctx c = c0;
   c.lane = opaque(c0.lane);
@@ -262,15 +276,22 @@ __device__ __forceinline__ void tile_step(const Ctx &c0, int t, int ntiles, Wave
     issue_tile<NB>(c, slots, ok_next);
   }
   int64_t slot_vec = -1;
-  if (t + 2 < ntiles) slot_vec = fetch_slots_vec(c, t + 2);
+  // Unconditional: past the split every lane yields -1 without a load, and consuming the value
+  // on every path keeps the compiler from treating it as pending (and waiting on the DMAs).
+  slot_vec = fetch_slots_vec(c, t + 2);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- S^T[key][row]: A = key rows (LDS), B = query rows (registers). Logical unit
-  // 2*kc + half of row `col` is stored at unit (2*kc + half) ^ swizzle.
+  // 2*kc + half of row `col` is stored at unit (2*kc + half) ^ swizzle. Even and odd
+  // fragments accumulate into two chains so that consecutive MFMAs are independent.
   f32x16 sacc;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
   {
+    f32x16 sodd;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sacc[e] = 0.f;
+      sodd[e] = 0.f;
+    }
     const char *lat = raw_buf<B>() + c.col * kLatRow;
     const int y = lat_swz(c.col) ^ c.half;
     const char *rope = raw_buf<B>() + kLatTile + c.col * kRopeRow;
@@ -281,61 +302,79 @@ __device__ __forceinline__ void tile_step(const Ctx &c0, int t, int ntiles, Wave
                                                 16 * ((2 * (kc & 7)) ^ y));
       return reinterpret_cast<const bf16x8 *>(rope + 16 * ((2 * (kc - kLatFrags)) ^ yr));
     };
-    bf16x8 kf[4];
+    // kKPrefetch fragment reads in flight: with one wave per SIMD nothing else hides the LDS
+    // latency
+    bf16x8 kf[kKPrefetch + 1];
 #pragma unroll
-    for (int kc = 0; kc < 3; ++kc) kf[kc] = *kaddr(kc);
+    for (int kc = 0; kc < kKPrefetch; ++kc) kf[kc] = *kaddr(kc);
 #pragma unroll
     for (int kc = 0; kc < kQFrags; ++kc) {
-      if (kc + 3 < kQFrags) kf[(kc + 3) & 3] = *kaddr(kc + 3);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc & 3], qf[kc], sacc, 0, 0, 0);
+      if (kc + kKPrefetch < kQFrags)
+        kf[(kc + kKPrefetch) % (kKPrefetch + 1)] = *kaddr(kc + kKPrefetch);
+      if (kc & 1)
+        sodd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc % (kKPrefetch + 1)], qf[kc],
+                                                       sodd, 0, 0, 0);
+      else
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc % (kKPrefetch + 1)], qf[kc],
+                                                       sacc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] += sodd[e];
   }
 
-  // ---- scores in log2 units; invisible keys -> -inf. Accumulator e holds key
-  // kb + 8*(e/4) + 4*half + e%4 of row `col`.
+  // ---- raw scores; invisible keys -> -inf. Accumulator e holds key kb + 8*(e/4) +
+  // 4*half + e%4 of row `col`. Masking is skipped for tiles of usable prefix keys only.
   const int kb = c.k0 + t * kTK;
   const uint32_t okbits = g_okbits[B];
   const bool tail = kb + kTK > c.P;
-  uint32_t tree_vis = 0xffffffffu;
-  if (tail) {
-    // the lane's row's mask bytes (addresses clamped into the row; keys past the split are
-    // already unusable in okbits)
-    uint8_t mb[16];
+  if (tail || okbits != 0xffffffffu) {
+    uint32_t tree_vis = 0xffffffffu;
+    if (tail) {
+      // the lane's row's mask bytes (addresses clamped into the row; keys past the split
+      // are already unusable in okbits)
+      uint8_t mb[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = kb + 8 * (e >> 2) + 4 * c.half + (e & 3);
-      mb[e] = mrow[min(j, c.k1 - 1)];
+      for (int e = 0; e < 16; ++e) {
+        const int j = kb + 8 * (e >> 2) + 4 * c.half + (e & 3);
+        mb[e] = mseg[moff + uint32_t(min(j, c.k1 - 1))];
+      }
+      tree_vis = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = kb + 8 * (e >> 2) + 4 * c.half + (e & 3);
+        tree_vis |= uint32_t(j < c.P || (row_ok && mb[e] != 0)) << e;
+      }
     }
-    tree_vis = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int j = kb + 8 * (e >> 2) + 4 * c.half + (e & 3);
-      tree_vis |= uint32_t(j < c.P || (row_ok && mb[e] != 0)) << e;
+      const int kk = 8 * (e >> 2) + 4 * c.half + (e & 3);
+      const bool vis = ((okbits >> kk) & 1u) && ((tree_vis >> e) & 1u);
+      sacc[e] = vis ? sacc[e] : -INFINITY;
     }
   }
-  float tmax = -INFINITY;
+  // max of the raw scores (the scale is positive, so it keeps the order), then the lane
+  // pair holding the other 16 keys of the row
+  float tmax;
   int targ = 0x7fffffff;
+  if (kArgmax) {
+    tmax = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int kk = 8 * (e >> 2) + 4 * c.half + (e & 3);
-    const bool vis = ((okbits >> kk) & 1u) && ((tree_vis >> e) & 1u);
-    const float v = vis ? sacc[e] * c2 : -INFINITY;
-    sacc[e] = v;
-    if (kArgmax) {
-      if (v > tmax) { tmax = v; targ = kb + kk; }
-    } else {
-      tmax = fmaxf(tmax, v);
+    for (int e = 0; e < 16; ++e) {
+      const int kk = 8 * (e >> 2) + 4 * c.half + (e & 3);
+      if (sacc[e] > tmax) { tmax = sacc[e]; targ = kb + kk; }
     }
-  }
-  {
-    const float om = swap_halves(tmax);
-    if (kArgmax) {
-      const int oj = swap_halves(targ);
-      if (om > tmax || (om == tmax && oj < targ)) targ = oj;
-    }
+    const float om = other_half(tmax);
+    const int oj = other_half(targ);
+    if (om > tmax || (om == tmax && oj < targ)) targ = oj;
     tmax = fmaxf(tmax, om);
+  } else {
+    tmax = sacc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
+    tmax = fmaxf(tmax, other_half(tmax));
   }
+  tmax *= c2;  // log2 units
   if (kArgmax && tmax > st.mx) st.best_j = targ;
   st.mx = fmaxf(st.mx, tmax);
 
@@ -348,30 +387,29 @@ __device__ __forceinline__ void tile_step(const Ctx &c0, int t, int ntiles, Wave
 #pragma unroll
     for (int d = 0; d < kDBlocks; ++d) scale_acc(o[d], alpha);
   }
-  const float msafe = st.m == -INFINITY ? 0.f : st.m;
+  const float negm = st.m == -INFINITY ? 0.f : -st.m;
 
-  // ---- P = exp2(s - m) rounded to fp16; the denominator sums the rounded values
+  // ---- P = exp2(s*c2 - m) rounded to nearest-even fp16 (v_cvt_pk_f16_f32: unbiased, so the
+  // denominator summed from the rounded values does not drift); the sum uses v_dot2
   f16x8 pf[2];
+  {
+    const f16x2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-  for (int ch = 0; ch < 2; ++ch) {
+    for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      f32x2 p;
-      p.x = __builtin_amdgcn_exp2f(sacc[8 * ch + e] - msafe);
-      p.y = __builtin_amdgcn_exp2f(sacc[8 * ch + e + 1] - msafe);
-      // round to nearest even (v_cvt_pk_f16_f32): unbiased, so the denominator summed from
-      // the rounded values does not drift low
-      const f16x2v h = __builtin_convertvector(p, f16x2v);
-      st.lsum += float(h.x) + float(h.y);
-      pf[ch][e] = h.x;
-      pf[ch][e + 1] = h.y;
+      for (int e = 0; e < 8; e += 2) {
+        f32x2 p;
+        p.x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ch + e], c2, negm));
+        p.y = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ch + e + 1], c2, negm));
+        const f16x2v h = __builtin_convertvector(p, f16x2v);
+        st.lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, h),
+                                         __builtin_bit_cast(fp16x2, ones), st.lsum, false);
+        pf[ch][e] = h.x;
+        pf[ch][e + 1] = h.y;
+      }
     }
   }
 
-  // ---- this thread's loads of tile t+1 (and the slots of t+2) have landed: convert them
-  // while P V runs
-  if (have_next) wait_tile_loads();
-  if (t + 2 < ntiles) slots_to_sgpr(slot_vec, slots);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- O^T[dim][row] += V^T[dim][key] P^T[key][row]. Key slot 8*half + 4*rr + e of chunk ch
@@ -392,24 +430,31 @@ __device__ __forceinline__ void tile_step(const Ctx &c0, int t, int ntiles, Wave
       }
       return vf;
     };
-    f16x8 vq[3];
-    vq[0] = vfrag(0, 0);
-    vq[1] = vfrag(0, 1);
+    f16x8 vq[kVPrefetch + 1];
+#pragma unroll
+    for (int it = 0; it < kVPrefetch; ++it) vq[it] = vfrag(it / kDBlocks, it % kDBlocks);
 #pragma unroll
     for (int it = 0; it < 2 * kDBlocks; ++it) {
       const int ch = it / kDBlocks, d = it % kDBlocks;
-      if (it + 2 < 2 * kDBlocks) {
-        const int it2 = it + 2;
-        vq[it2 % 3] = vfrag(it2 / kDBlocks, it2 % kDBlocks);
+      if (it + kVPrefetch < 2 * kDBlocks) {
+        const int it2 = it + kVPrefetch;
+        vq[it2 % (kVPrefetch + 1)] = vfrag(it2 / kDBlocks, it2 % kDBlocks);
       }
-      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[it % 3], pf[ch], o[d], 0, 0, 0);
+      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[it % (kVPrefetch + 1)], pf[ch], o[d], 0,
+                                                    0, 0);
       pin_agpr(o[d]);
-      // unconditional (branch-free so it interleaves; with no next tile it writes zeros into
-      // the idle buffer)
-      if ((it & 3) == 3) convert_unit<NB>(c, it >> 2, ok_next);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+
+  // ---- end of the tile: this thread's loads of tile t+1 (and the slots of t+2) have had the
+  // whole tile to land; convert them to the fp16 latent tile, then publish with the barrier
+  if (have_next) {
+    wait_tile_loads();
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) convert_unit<NB>(c, i, ok_next);
+  }
+  slots_to_sgpr(slot_vec, slots);
 
   if (have_next && c.lane == 0)
     reinterpret_cast<uint8_t *>(&g_okbits[NB])[c.wave] = uint8_t(ok_next);
@@ -471,7 +516,7 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
     slots_to_sgpr(fetch_slots_vec(c, 0), slots);
     ok0 = wave_ok_bits(c, 0, slots);
     issue_tile<0>(c, slots, ok0);
-    if (ntiles > 1) slot_vec = fetch_slots_vec(c, 1);
+    slot_vec = fetch_slots_vec(c, 1);
   }
 
   // query fragments (B operand): row `col`, dims 16*kc + 8*half .. +8
@@ -501,11 +546,14 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   st.lsum = 0.f;
   st.best_j = -1;
   const float c2 = a.scale * kLog2e;
-  const uint8_t *mrow = a.mask + seg.m0 + int64_t(tok) * seg.L;
+  // the row's mask bytes: a request-uniform base plus a 32-bit lane offset (a request's mask
+  // segment is validated to stay under 2 GiB)
+  const uint8_t *mseg = a.mask + seg.m0;
+  const uint32_t moff = uint32_t(tok) * uint32_t(seg.L);
 
   if (ntiles > 0) {
     wait_tile_loads();
-    if (ntiles > 1) slots_to_sgpr(slot_vec, slots);
+    slots_to_sgpr(slot_vec, slots);
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) convert_unit<0>(c, i, ok0);
     if (c.lane == 0) reinterpret_cast<uint8_t *>(&g_okbits[0])[c.wave] = uint8_t(ok0);
@@ -513,9 +561,9 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   __syncthreads();
 
   for (int t = 0; t < ntiles; t += 2) {
-    tile_step<0, kArgmax>(c, t, ntiles, slots, qf, o, st, c2, row_ok, mrow);
+    tile_step<0, kArgmax>(c, t, ntiles, slots, qf, o, st, c2, row_ok, mseg, moff);
     if (t + 1 < ntiles)
-      tile_step<1, kArgmax>(c, t + 1, ntiles, slots, qf, o, st, c2, row_ok, mrow);
+      tile_step<1, kArgmax>(c, t + 1, ntiles, slots, qf, o, st, c2, row_ok, mseg, moff);
   }
 
   // ---- write the partial of this split

@@ -76,3 +76,15 @@ def test_tokens_not_covered_by_qo_indptr(kernel):
     ref = run_oracle(w)
     compare(w, (o[:5].reshape(-1, 512).astype(np.float64), lse.cpu().numpy()[:5].ravel(), None,
                 0), ref)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_non_positive_scale_is_rejected(kernel):
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+    w = wl.build_workload("scale", np.random.default_rng(24), 4, [8], [2], 32)
+    dev = to_device(w)
+    for bad in (0.0, -0.5, float("inf"), float("nan")):
+        w.scale = bad
+        with pytest.raises(B.VerifyAttnError) as e:
+            run_gpu(w, kernel=kernel, dev=dev)
+        assert e.value.status == B.VA_ERR_INVALID
