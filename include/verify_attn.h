@@ -99,7 +99,9 @@ typedef struct {
   int64_t max_q_tokens;   /* upper bound on num_tokens                                     */
   int32_t num_splits;     /* key splits per request (1..256); 0 = chosen from the bounds    */
   int32_t kernel;         /* VA_KERNEL_*                                                   */
-  void *workspace;        /* device memory, 256-byte aligned, or NULL: allocated at create */
+  void *workspace;        /* device memory, 256-byte aligned, or NULL: allocated at create.
+                             Owned by the context until verify_attn_destroy: the caller must
+                             not write it (its first bytes are set once, at create) */
   size_t workspace_bytes; /* size of `workspace` when it is not NULL                        */
 } verify_attn_config;
 
@@ -114,8 +116,8 @@ typedef struct {
 /* Workspace bytes a config needs (0 if the config is invalid). */
 size_t verify_attn_workspace_bytes(const verify_attn_config *cfg);
 
-/* Validates `cfg`, binds or allocates the workspace, clears the status word (synchronously,
- * on the null stream). Returns VA_OK and sets *out, or an error and leaves *out NULL. */
+/* Validates `cfg`, binds or allocates the workspace, clears its status words and a row of
+ * zeros the kernels read in place of unusable key rows (synchronously, on the null stream). Returns VA_OK and sets *out, or an error and leaves *out NULL. */
 va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **out);
 
 /*

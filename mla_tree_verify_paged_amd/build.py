@@ -17,6 +17,9 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix instructions written by the compiler keep their accumulators in VGPRs; the
+    # partial kernel's output accumulators are placed in AGPRs by hand
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -117,6 +117,7 @@ void bind_workspace(verify_attn_ctx *x) {
   va::workspace_layout(x->splits, rows_cap, off);
   char *b = static_cast<char *>(x->ws_base);
   x->ws.status = reinterpret_cast<uint32_t *>(b + off[0]);
+  x->ws.zero_row = reinterpret_cast<const uint16_t *>(b + off[0] + va::kZeroRowOffset);
   x->ws.part_o = reinterpret_cast<float *>(b + off[1]);
   x->ws.part_lse = reinterpret_cast<float *>(b + off[2]);
   x->ws.part_max = reinterpret_cast<float *>(b + off[3]);
@@ -157,7 +158,7 @@ va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **ou
       return fail(VA_ERR_HIP, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
     owned = true;
   }
-  hipError_t e = hipMemset(base, 0, 256);  // status word
+  hipError_t e = hipMemset(base, 0, va::kHeaderBytes);  // status words and the zero row
   if (e != hipSuccess) {
     if (owned) (void)hipFree(base);
     return fail(VA_ERR_HIP, "hipMemset failed: %s", hipGetErrorString(e));

@@ -2,6 +2,7 @@
 //
 // Workspace layout (all offsets 256-byte aligned), for S splits and R = max_q_tokens * H rows:
 //   status   uint32 [64]            sticky VA_DEV_* bits in word 0
+//   zero_row uint16 [576]           zeros; key rows that must not be read load from here
 //   part_o   float  [S][R][512]     per-split normalised output O_s
 //   part_lse float  [S][R]          per-split log-sum-exp (natural log); -inf for an empty split
 //   part_max float  [S][R]          per-split max score (natural-log units)
@@ -23,6 +24,7 @@ constexpr int kMaxSplits = 256;
 
 struct Workspace {
   uint32_t *status;
+  const uint16_t *zero_row;
   float *part_o;
   float *part_lse;
   float *part_max;
@@ -57,10 +59,15 @@ struct RunArgs {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The status words and the zero row, set to zero when a context is created.
+constexpr size_t kStatusBytes = 64 * sizeof(uint32_t);
+constexpr size_t kZeroRowOffset = kStatusBytes;
+constexpr size_t kHeaderBytes = kZeroRowOffset + kDim * sizeof(uint16_t);
+
 // Byte offsets of the workspace regions for S splits and R rows; returns the total size.
 inline size_t workspace_layout(int32_t S, int64_t R, size_t off[5]) {
   size_t o = 0;
-  off[0] = o; o = align256(o + 64 * sizeof(uint32_t));
+  off[0] = o; o = align256(o + kHeaderBytes);
   off[1] = o; o = align256(o + size_t(S) * size_t(R) * kLatent * sizeof(float));
   off[2] = o; o = align256(o + size_t(S) * size_t(R) * sizeof(float));
   off[3] = o; o = align256(o + size_t(S) * size_t(R) * sizeof(float));

@@ -12,23 +12,31 @@
 //  * a workgroup of 4 wavefronts owns 128 (token, head) rows - with H=64 every head of two
 //    tree tokens - so one LDS copy of a key tile serves 128 rows;
 //  * key tiles (32 paged latent rows) arrive in LDS by direct global->LDS 16-byte loads
-//    (global_load_lds_dwordx4), one tile ahead of the compute, without passing through
-//    registers: one load instruction moves the 1 KB latent part of one row, so the row and
-//    its slot are wave-uniform and the slots come in through scalar loads. Rows are stored
-//    XOR-swizzled in 16-byte units so the K-fragment reads are free of LDS bank conflicts;
+//    (global_load_lds_dwordx4), two tiles ahead of their products, without passing through
+//    registers: one load instruction moves the 1 KB latent part of one row from a scalar
+//    base address, so a row costs one instruction plus its slot's address. Latent rows sit
+//    at a padded 1040-byte stride and rope units are placed by a lane permutation, so every
+//    matrix-operand read is bank-conflict free and is one base register plus an immediate;
 //  * S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16: A = key rows from LDS, B = the wave's 32
 //    query rows held in registers. The accumulator gives each lane one row and 16 keys, so a
 //    softmax row reduction is one cross-lane swap;
-//  * P is rounded (to nearest even) to fp16 and O^T += V^T P^T runs on v_mfma_f32_32x32x16_f16. V is the first
-//    512 dims of the same rows, converted to fp16 by the thread that loaded each unit while
-//    the previous tile's products run, and read as V^T fragments with ds_read_b64_tr_b16.
-//    The P fragment is the S accumulator itself: key slots are permuted the same way in both
-//    operands;
+//  * P is rounded (to nearest even) to fp16 and O^T += V^T P^T runs on
+//    v_mfma_f32_32x32x16_f16. V is the first 512 dims of the same rows, converted to fp16 once
+//    per tile (each thread converts the units it loaded) and read as V^T fragments with
+//    ds_read_b64_tr_b16. The P fragment is the S accumulator itself: key slots are permuted
+//    the same way in both operands;
+//  * the tile loop is software-pipelined: the P.V products of tile t are interleaved with the
+//    QK^T products of tile t+1 (so consecutive matrix instructions are independent), with the
+//    fp16 conversion of tile t+1 and the loads of tile t+2 slotted between them. With one
+//    wavefront per SIMD (the 256 output accumulators per lane rule out more) every issued
+//    instruction costs issue time, so the loop is written to issue as few as possible;
 //  * the running max is rescaled lazily (only when it grows by more than 2^8), in place in
 //    the accumulation registers, so the 256 fp32 accumulators per lane never leave them;
 //  * workgroups are mapped so that all row tiles of one key split run on the same XCD and
 //    share its L2; HBM then sees each latent row about once.
 #include <math.h>
+
+#include <type_traits>
 
 #include "va_internal.h"
 
@@ -41,6 +49,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__fp16)))) __fp16 fp16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
@@ -50,38 +59,34 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kRows = kMfmaRowsPerBlock;    // 128 rows = 4 waves x 32
 constexpr int kTK = 32;                     // keys per tile
 constexpr int kRowsPerWave = kTK / kWaves;  // 8 key rows staged by each wave
-constexpr int kLatRow = kLatent * 2;        // 1024 bytes of latent per key row
-constexpr int kRopeRow = kRope * 2;         // 128 bytes of rope per key row
-constexpr int kLatTile = kTK * kLatRow;     // 32 KB
-constexpr int kRawTile = kLatTile + kTK * kRopeRow;  // + 4 KB = 36 KB
-constexpr int kVRow = kLatent * 2 + 64;     // fp16 V tile row stride: 1088 bytes
-constexpr int kVTile = kTK * kVRow;         // 34,816 bytes
+constexpr int kLatStride = 2 * kLatent + 16;             // 1040-byte latent row (padded)
+constexpr int kRopeOff = kTK * kLatStride;               // 33,280: rope block of a raw tile
+constexpr int kRawTile = kRopeOff + kTK * 2 * kRope;     // + 4 KB = 37,376
+constexpr int kVRow = 2 * kLatent + 64;                  // fp16 V tile row stride: 1088
+constexpr int kVTile = kTK * kVRow;                      // 34,816
+constexpr int kVOff = 2 * kRawTile;                      // the two fp16 tiles follow
+constexpr int kLdsBytes = kVOff + 2 * kVTile;            // 144,384
 constexpr int kQFrags = kDim / 16;          // 36 bf16x8 B-operand fragments per lane
 constexpr int kLatFrags = kLatent / 16;     // the first 32 of them are latent dims
 constexpr int kDBlocks = kLatent / 32;      // 16 output dim blocks of 32
+constexpr int kNumPV = 2 * kDBlocks;        // 32 P.V products per tile
+constexpr int kDepth = 6;                   // operand fragment reads in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;            // lazy-rescale threshold (log2 units)
-constexpr int kKPrefetch = 7;               // K-fragment LDS reads kept in flight per wave
-constexpr int kVPrefetch = 8;               // V-fragment (pairs of transposed) reads in flight
 
 static_assert(kRowsPerWave == 8, "one rope load instruction covers 8 rows");
+static_assert(kRawTile % 16 == 0 && kVOff % 16 == 0, "16-byte aligned tiles");
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
-// LDS: two tile buffers, each a raw bf16 tile (latent rows, then rope rows, both swizzled)
-// plus its fp16 latent copy; and the usable-key bits of the tiles in flight (a byte per wave).
-__shared__ __attribute__((aligned(16))) char g_raw0[kRawTile];
-__shared__ __attribute__((aligned(16))) char g_raw1[kRawTile];
-__shared__ __attribute__((aligned(16))) char g_v0[kVTile];
-__shared__ __attribute__((aligned(16))) char g_v1[kVTile];
+// LDS: raw bf16 tiles 0 and 1 (latent rows at a padded stride, then the rope block), then
+// fp16 latent tiles 0 and 1; the usable-key bits of the two raw tiles (a byte per wave).
+__shared__ __attribute__((aligned(16))) char g_lds[kLdsBytes];
 __shared__ uint32_t g_okbits[2];
 
-template <int B> __device__ __forceinline__ char *raw_buf() { return B ? g_raw1 : g_raw0; }
-template <int B> __device__ __forceinline__ char *v_buf() { return B ? g_v1 : g_v0; }
-
-// Swizzles (16-byte unit index within a row): latent units XOR (row & 15), rope units XOR
-// ((row >> 1) & 7). Both keep a unit inside its aligned group.
-__device__ __forceinline__ int lat_swz(int row) { return row & 15; }
-__device__ __forceinline__ int rope_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+  return uint32_t(reinterpret_cast<uintptr_t>(p));
+}
 
 __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
   const float lo = __uint_as_float(w << 16);
@@ -90,7 +95,6 @@ __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
 }
 
 __device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
-__device__ __forceinline__ int swap_halves(int v) { return __shfl_xor(v, 32, 64); }
 
 // The value lane l ^ 32 holds (v_permlane32_swap, no LDS round trip).
 __device__ __forceinline__ int other_half(int v) {
@@ -107,8 +111,19 @@ __device__ __forceinline__ float other_half(float v) {
 // (Empty inline assembly with a register-class constraint; it emits no instruction.)
 __device__ __forceinline__ void pin_agpr(f32x16 &x) { asm volatile("" : "+a"(x)); }
 
+// O^T block += A (fp16 V^T fragment) x B (fp16 P^T fragment), accumulating in AGPRs. Written
+// as assembly because the library is compiled with matrix instructions in their VGPR form (the
+// score accumulator must not take AGPRs, which the 256 output accumulators fill). The compiler
+// does not see this as a matrix instruction: its operands arrive through ordinary waits (A
+// from LDS reads, B long before from VALU), and every VALU read of acc is preceded by
+// matrix_drain().
+__device__ __forceinline__ void pv_mfma(f32x16 &acc, const u32x4 &a, const f16x8 &b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // acc *= alpha, element by element, without moving the accumulator out of the registers the
-// matrix instructions accumulate in.
+// matrix instructions accumulate in. The caller separates this from the matrix instructions
+// that write acc (the compiler does not see into the assembly).
 __device__ __forceinline__ void scale_acc(f32x16 &acc, float alpha) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -124,18 +139,33 @@ __device__ __forceinline__ void scale_acc(f32x16 &acc, float alpha) {
   }
 }
 
-// One global_load_lds_dwordx4: each lane's 16 bytes at `src` land at lds_dst + 16*lane
-// (lds_dst wave-uniform). Issued as inline assembly so that the compiler does not track the
-// LDS write (it would otherwise wait for these loads before every LDS read of the other tile
-// buffer); the kernel waits for them itself before the data is read, and a barrier orders
-// them for the other wavefronts.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds_dst) {
+// Wait states around the in-place rescale: enough for the longest matrix instruction to
+// retire before its accumulator is read, and for the rewritten values before the next use.
+__device__ __forceinline__ void matrix_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// One global_load_lds_dwordx4 from a scalar base: lane l's 16 bytes at base + voff land at
+// lds + 16*l. Inline assembly so that the compiler does not track the LDS write (it would
+// otherwise wait for these loads before every LDS read); the kernel waits for them itself
+// before the data is read, and a barrier orders them for the other wavefronts.
+__device__ __forceinline__ void dma_row(uint64_t base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+// The same from a per-lane 64-bit address.
+__device__ __forceinline__ void dma_lanes(const void *src, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
-      : "v"(src), "s"(lds_dst)
+      : "v"(src), "s"(lds)
       : "memory", "m0");
 }
 
@@ -145,18 +175,11 @@ __device__ __forceinline__ void wait_tile_loads() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Returns v unchanged, but hides its value from the optimiser so that address arithmetic
-// derived from it is recomputed where it is used rather than hoisted out of the tile loop
-// and kept live (register pressure is the binding constraint of this kernel).
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
 // Per-workgroup constants of one split.
 struct Ctx {
   const uint16_t *kv;
   const int64_t *kvi;   // kv_indices of the request
+  const uint16_t *zero; // a row of zeros
   int64_t num_slots;
   uint32_t *status;
   int k0, k1, P;
@@ -164,87 +187,76 @@ struct Ctx {
   int lane, half, col;
 };
 
-// The slots of the 8 key rows a wave stages for one tile (wave-uniform, in SGPRs).
-struct WaveSlots {
-  int64_t s[kRowsPerWave];
-};
-
-// Lane i < 8 loads the slot of row 8*wave + i of tile t (-1 past the split). A vector-memory
-// load on purpose: it completes in order with the tile loads and is consumed after the wait
-// for them, so it never stalls anything on its own.
-__device__ __forceinline__ int64_t fetch_slots_vec(const Ctx &c, int t) {
+// Lane l fetches the slot of row (l & 7) of its wave's 8 rows of tile t (-1 past the split,
+// without a load). Consumed a tile later, after the wait for the tile loads.
+__device__ __forceinline__ int64_t fetch_slot(const Ctx &c, int t) {
   int64_t v = -1;
-  const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + c.lane;
-  if (c.lane < kRowsPerWave && j < c.k1) v = c.kvi[j];
+  const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane & 7);
+  if (j < c.k1) v = c.kvi[j];
   return v;
 }
 
-__device__ __forceinline__ void slots_to_sgpr(int64_t v, WaveSlots &ws) {
-  const int lo = int(uint64_t(v)), hi = int(uint64_t(v) >> 32);
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const uint32_t l = uint32_t(__builtin_amdgcn_readlane(lo, i));
-    const uint32_t h = uint32_t(__builtin_amdgcn_readlane(hi, i));
-    ws.s[i] = int64_t((uint64_t(h) << 32) | l);
-  }
+// The loads of one tile, prepared from the fetched slots: the row address each lane holds
+// (row l & 7; the zero row for keys past the split or slots out of range) and the wave's
+// usable-row bits.
+struct TileLoads {
+  uint64_t addr;
+  uint32_t ok;   // bit i: row i of this wave is a usable key
+};
+
+__device__ __forceinline__ TileLoads plan_tile(const Ctx &c, int t, int64_t slot) {
+  const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane & 7);
+  const bool in = j < c.k1;
+  const bool valid = in && slot >= 0 && slot < c.num_slots;
+  TileLoads tl;
+  tl.ok = uint32_t(__ballot(valid)) & 0xffu;
+  if (__ballot(in && !valid) != 0 && c.lane == 0) atomicOr(c.status, 1u);  // VA_DEV_SLOT_RANGE
+  const uint64_t row = uint64_t(reinterpret_cast<uintptr_t>(c.kv)) + uint64_t(slot) * (2 * kDim);
+  tl.addr = valid ? row : uint64_t(reinterpret_cast<uintptr_t>(c.zero));
+  return tl;
 }
 
-// Usable-key bits of the wave's rows: -1 marks a row past the split; a slot out of range is
-// flagged and unusable.
-__device__ __forceinline__ uint32_t wave_ok_bits(const Ctx &c, int t, const WaveSlots &ws) {
-  uint32_t ok = 0;
-  bool bad = false;
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + i;
-    const bool in = j < c.k1;
-    const bool valid = ws.s[i] >= 0 && ws.s[i] < c.num_slots;
-    bad |= in && !valid;
-    ok |= uint32_t(in && valid) << i;
-  }
-  if (bad && c.lane == 0) atomicOr(c.status, 1u);  // VA_DEV_SLOT_RANGE
-  return ok;
+// Latent row i of the wave: one 64-lane load of its 1 KB into the padded row.
+__device__ __forceinline__ void issue_latent(const Ctx &c, const TileLoads &tl, uint32_t raw,
+                                             int i) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(tl.addr)), i));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(tl.addr >> 32)), i));
+  const uint64_t base = (uint64_t(hi) << 32) | lo;
+  dma_row(base, uint32_t(16 * c.lane), raw + (c.wave * kRowsPerWave + i) * kLatStride);
 }
 
-// Direct global->LDS loads of the wave's 8 rows of a tile into raw buffer B: per row one
-// 64-lane load of the 1 KB latent part (lane = stored unit, loading logical unit
-// lane ^ swizzle), and one load for the rope parts of all 8 rows (8 lanes per row).
-template <int B>
-__device__ __forceinline__ void issue_tile(const Ctx &c, const WaveSlots &ws, uint32_t ok) {
-  const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(raw_buf<B>()));
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int row = c.wave * kRowsPerWave + i;
-    const int64_t sl = ((ok >> i) & 1u) ? ws.s[i] : 0;
-    const uint16_t *src = c.kv + sl * kDim + 8 * (c.lane ^ lat_swz(row));
-    dma16(src, base + row * kLatRow);
-  }
-  {
-    const int q = c.lane & 7, ri = c.lane >> 3;
-    const int row = c.wave * kRowsPerWave + ri;
-    int64_t sl = 0;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i)
-      if (ri == i && ((ok >> i) & 1u)) sl = ws.s[i];
-    const uint16_t *src = c.kv + sl * kDim + kLatent + 8 * (q ^ rope_swz(row));
-    dma16(src, base + kLatTile + c.wave * (kRowsPerWave * kRopeRow));
-  }
+// The rope parts of the wave's 8 rows: lane l loads unit u of row l & 7 into position l of
+// the wave's 1 KB rope block, with u = 2*(l >> 4) + (((l >> 3) & 1) ^ (wave & 1)).
+__device__ __forceinline__ void issue_rope(const Ctx &c, const TileLoads &tl, uint32_t raw) {
+  const int u = 2 * (c.lane >> 4) + (((c.lane >> 3) & 1) ^ (c.wave & 1));
+  const char *src = reinterpret_cast<const char *>(uintptr_t(tl.addr)) + 2 * kLatent + 16 * u;
+  dma_lanes(src, raw + kRopeOff + c.wave * 1024);
 }
 
-// fp16 copy of the latent unit this thread loaded for row i of its wave (zeros if unusable).
-template <int B>
-__device__ __forceinline__ void convert_unit(const Ctx &c, int i, uint32_t ok) {
-  const int row = c.wave * kRowsPerWave + i;
-  const uint4 x = *reinterpret_cast<const uint4 *>(raw_buf<B>() + row * kLatRow + 16 * c.lane);
-  uint4 h = make_uint4(0, 0, 0, 0);
-  if ((ok >> i) & 1u) {
-    h.x = bf16pair_to_f16pair(x.x);
-    h.y = bf16pair_to_f16pair(x.y);
-    h.z = bf16pair_to_f16pair(x.z);
-    h.w = bf16pair_to_f16pair(x.w);
-  }
-  const int unit = c.lane ^ lat_swz(row);
-  *reinterpret_cast<uint4 *>(v_buf<B>() + row * kVRow + 16 * unit) = h;
+__device__ __forceinline__ void publish_ok(const Ctx &c, int buf, uint32_t ok) {
+  if (c.lane == 0) reinterpret_cast<uint8_t *>(&g_okbits[buf])[c.wave] = uint8_t(ok);
+}
+
+// Per-lane byte offsets (relative to a tile buffer) of the operand reads.
+struct LaneOffs {
+  uint32_t k_lat;   // K fragment kc < 32: + 32*kc
+  uint32_t k_rope;  // K fragment 32 + j: + 256*j
+  uint32_t v_tr;    // V^T fragment (chunk ch, half rr, dim block d): + (16ch+8rr)*1088 + 64d
+  uint32_t cv_rd;   // conversion read of unit `lane` of the wave's row i: + 1040*i
+  uint32_t cv_wr;   // conversion write: + 1088*i
+};
+
+__device__ __forceinline__ LaneOffs lane_offsets(const Ctx &c) {
+  LaneOffs lo;
+  const int row = c.col;
+  lo.k_lat = row * kLatStride + 16 * c.half;
+  lo.k_rope = kRopeOff + 1024 * (row >> 3) + 128 * (c.half ^ ((row >> 3) & 1)) + 16 * (row & 7);
+  const int g = c.lane & 15;
+  const int m0 = 16 * ((c.lane >> 4) & 1);
+  lo.v_tr = (4 * c.half + (g >> 2)) * kVRow + (m0 + 4 * (g & 3)) * 2;
+  lo.cv_rd = c.wave * kRowsPerWave * kLatStride + 16 * c.lane;
+  lo.cv_wr = c.wave * kRowsPerWave * kVRow + 16 * c.lane;
+  return lo;
 }
 
 // Running per-lane state of the online softmax.
@@ -255,78 +267,129 @@ struct RowState {
   int best_j;   // argmax key position
 };
 
-// One key tile t in buffer B: QK^T, mask, online softmax, PV. Tile t+1 is loaded into buffer
-// B^1 meanwhile (issued first, waited for and converted last), and the slots of tile t+2 are
-// fetched.
-template <int B, bool kArgmax>
-__device__ __forceinline__ void tile_step(const Ctx &c0, int t, int ntiles, WaveSlots &slots,
-                                          const bf16x8 *qf, f32x16 *o, RowState &st, float c2,
-                                          bool row_ok, const uint8_t *mseg, uint32_t moff) {
-  constexpr int NB = B ^ 1;
-  Ctx c = c0;
-  c.lane = opaque(c0.lane);
-  c.col = c.lane & 31;
-  c.half = c.lane >> 5;
-
-  // ---- tile t+1: usable bits, loads into buffer B^1; then the slots of tile t+2
-  const bool have_next = t + 1 < ntiles;
-  uint32_t ok_next = 0;
-  if (have_next) {
-    ok_next = wave_ok_bits(c, t + 1, slots);
-    issue_tile<NB>(c, slots, ok_next);
+// ---- the matrix phase of one pipeline step
+// Operation p of the step: with both products, QK_0 PV_0 QK_1 PV_1 ... QK_31 PV_31 QK_32..35;
+// otherwise the one product's operations in order.
+template <bool QK, bool PV> struct Sched {
+  static constexpr int kOps = (QK ? kQFrags : 0) + (PV ? kNumPV : 0);
+  static constexpr bool is_pv(int p) { return QK && PV ? (p < 2 * kNumPV && (p & 1)) : PV; }
+  static constexpr int index(int p) {
+    return QK && PV ? (p < 2 * kNumPV ? (p >> 1) : p - kNumPV) : p;
   }
-  int64_t slot_vec = -1;
-  // Unconditional: past the split every lane yields -1 without a load, and consuming the value
-  // on every path keeps the compiler from treating it as pending (and waiting on the DMAs).
-  slot_vec = fetch_slots_vec(c, t + 2);
-  __builtin_amdgcn_sched_barrier(0);
+  // conversion unit u: read after operation rd(u), converted and written after wr(u)
+  static constexpr int wr(int u) {
+    return QK && PV ? (u < 4 ? 49 + 4 * u : 60 + u) : 6 + 4 * u;
+  }
+  static constexpr int rd(int u) { return wr(u) - 2; }
+};
 
-  // ---- S^T[key][row]: A = key rows (LDS), B = query rows (registers). Logical unit
-  // 2*kc + half of row `col` is stored at unit (2*kc + half) ^ swizzle. Even and odd
-  // fragments accumulate into two chains so that consecutive MFMAs are independent.
-  f32x16 sacc;
-  {
-    f32x16 sodd;
+struct StepIO {
+  const char *kraw;   // raw tile read by QK (and by the conversion)
+  const char *vrd;    // fp16 tile read by PV
+  char *vwr;          // fp16 tile written by the conversion
+  uint32_t dma_raw;   // LDS address of the raw tile the loads fill
+};
+
+// Calls f(std::integral_constant<int, I>) for I = I0 .. N-1, unrolled at compile time.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <bool QK, bool PV, bool kLoads>
+__device__ __forceinline__ void matrix_step(const Ctx &c, const LaneOffs &lo, const StepIO &io,
+                                            const TileLoads &tl, const bf16x8 *qf, f32x16 *o,
+                                            f32x16 &sacc, const f16x8 *pf) {
+  using S = Sched<QK, PV>;
+  constexpr int N = S::kOps;
+  const char *klat = io.kraw + lo.k_lat;
+  const char *krope = io.kraw + lo.k_rope;
+  const char *vtr = io.vrd + lo.v_tr;
+  const char *cvr = io.kraw + lo.cv_rd;
+  char *cvw = io.vwr + lo.cv_wr;
+
+  u32x4 fr[kDepth + 1];
+  u32x4 craw[kRowsPerWave];
+
+  // operand fragment of operation p
+  auto load = [&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    if constexpr (p < N) {
+      u32x4 r;
+      if constexpr (!S::is_pv(p)) {
+        constexpr int kc = S::index(p);
+        if constexpr (kc < kLatFrags)
+          r = *reinterpret_cast<const u32x4 *>(klat + 32 * kc);
+        else
+          r = *reinterpret_cast<const u32x4 *>(krope + 256 * (kc - kLatFrags));
+      } else {
+        constexpr int it = S::index(p), ch = it / kDBlocks, d = it % kDBlocks;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sacc[e] = 0.f;
-      sodd[e] = 0.f;
+        for (int rr = 0; rr < 2; ++rr) {
+          const fp16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+              (lds_fp16x4 *)(vtr + (16 * ch + 8 * rr) * kVRow + 64 * d));
+          const u32x2 w = __builtin_bit_cast(u32x2, x);
+          r[2 * rr] = w[0];
+          r[2 * rr + 1] = w[1];
+        }
+      }
+      fr[p % (kDepth + 1)] = r;
     }
-    const char *lat = raw_buf<B>() + c.col * kLatRow;
-    const int y = lat_swz(c.col) ^ c.half;
-    const char *rope = raw_buf<B>() + kLatTile + c.col * kRopeRow;
-    const int yr = rope_swz(c.col) ^ c.half;
-    auto kaddr = [&](int kc) -> const bf16x8 * {
-      if (kc < kLatFrags)
-        return reinterpret_cast<const bf16x8 *>(lat + 256 * (kc >> 3) +
-                                                16 * ((2 * (kc & 7)) ^ y));
-      return reinterpret_cast<const bf16x8 *>(rope + 16 * ((2 * (kc - kLatFrags)) ^ yr));
-    };
-    // kKPrefetch fragment reads in flight: with one wave per SIMD nothing else hides the LDS
-    // latency
-    bf16x8 kf[kKPrefetch + 1];
-#pragma unroll
-    for (int kc = 0; kc < kKPrefetch; ++kc) kf[kc] = *kaddr(kc);
-#pragma unroll
-    for (int kc = 0; kc < kQFrags; ++kc) {
-      if (kc + kKPrefetch < kQFrags)
-        kf[(kc + kKPrefetch) % (kKPrefetch + 1)] = *kaddr(kc + kKPrefetch);
-      if (kc & 1)
-        sodd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc % (kKPrefetch + 1)], qf[kc],
-                                                       sodd, 0, 0, 0);
-      else
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc % (kKPrefetch + 1)], qf[kc],
+  };
+
+  static_for<0, kDepth>(load);
+  static_for<0, N>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    load(std::integral_constant<int, p + kDepth>{});
+    const u32x4 a = fr[p % (kDepth + 1)];
+    if constexpr (S::is_pv(p)) {
+      constexpr int it = S::index(p), ch = it / kDBlocks, d = it % kDBlocks;
+      pv_mfma(o[d], a, pf[ch]);
+    } else {
+      constexpr int kc = S::index(p);
+      if constexpr (kc == 0) {
+        const f32x16 zero = {};
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kc],
+                                                       zero, 0, 0, 0);
+      } else {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kc],
                                                        sacc, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    // loads of the tile two steps ahead: 8 latent rows, then the rope block
+    if constexpr (kLoads) {
+      if constexpr (p >= 1 && p <= kRowsPerWave) issue_latent(c, tl, io.dma_raw, p - 1);
+      if constexpr (p == kRowsPerWave + 1) issue_rope(c, tl, io.dma_raw);
+    }
+    // fp16 copy of the latent units this thread loaded for the tile QK reads
+    if constexpr (QK) {
+      static_for<0, kRowsPerWave>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (p == S::rd(u))
+          craw[u] = *reinterpret_cast<const u32x4 *>(cvr + kLatStride * u);
+        if constexpr (p == S::wr(u)) {
+          u32x4 h;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[e] += sodd[e];
-  }
+          for (int e = 0; e < 4; ++e) h[e] = bf16pair_to_f16pair(craw[u][e]);
+          *reinterpret_cast<u32x4 *>(cvw + kVRow * u) = h;
+        }
+      });
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
 
-  // ---- raw scores; invisible keys -> -inf. Accumulator e holds key kb + 8*(e/4) +
-  // 4*half + e%4 of row `col`. Masking is skipped for tiles of usable prefix keys only.
-  const int kb = c.k0 + t * kTK;
-  const uint32_t okbits = g_okbits[B];
+// ---- softmax of one tile's scores (sacc): mask, max, lazy rescale, P = exp2 rounded to fp16
+template <bool kArgmax>
+__device__ __forceinline__ void softmax_tile(const Ctx &c, int kb, uint32_t okbits,
+                                             f32x16 &sacc, f32x16 *o, RowState &st, float c2,
+                                             bool row_ok, const uint8_t *mseg, uint32_t moff,
+                                             f16x8 *pf) {
+  // raw scores; invisible keys -> -inf. Accumulator e holds key kb + 8*(e/4) + 4*half + e%4
+  // of row `col`. Masking is skipped for tiles of usable prefix keys only.
   const bool tail = kb + kTK > c.P;
   if (tail || okbits != 0xffffffffu) {
     uint32_t tree_vis = 0xffffffffu;
@@ -378,87 +441,36 @@ __device__ __forceinline__ void tile_step(const Ctx &c0, int t, int ntiles, Wave
   if (kArgmax && tmax > st.mx) st.best_j = targ;
   st.mx = fmaxf(st.mx, tmax);
 
-  // ---- lazy rescale of the running max (rare after the first tile)
+  // lazy rescale of the running max (rare after the first tile)
   const bool need = tmax > st.m + kRescale;
   if (__any(need)) {
     const float alpha = need ? __builtin_amdgcn_exp2f(st.m - tmax) : 1.f;
     if (need) st.m = tmax;
     st.lsum *= alpha;
+    matrix_drain();
 #pragma unroll
     for (int d = 0; d < kDBlocks; ++d) scale_acc(o[d], alpha);
+    matrix_drain();
   }
   const float negm = st.m == -INFINITY ? 0.f : -st.m;
 
-  // ---- P = exp2(s*c2 - m) rounded to nearest-even fp16 (v_cvt_pk_f16_f32: unbiased, so the
+  // P = exp2(s*c2 - m) rounded to nearest-even fp16 (v_cvt_pk_f16_f32: unbiased, so the
   // denominator summed from the rounded values does not drift); the sum uses v_dot2
-  f16x8 pf[2];
-  {
-    const f16x2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+  const f16x2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
+  for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        f32x2 p;
-        p.x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ch + e], c2, negm));
-        p.y = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ch + e + 1], c2, negm));
-        const f16x2v h = __builtin_convertvector(p, f16x2v);
-        st.lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, h),
-                                         __builtin_bit_cast(fp16x2, ones), st.lsum, false);
-        pf[ch][e] = h.x;
-        pf[ch][e + 1] = h.y;
-      }
+    for (int e = 0; e < 8; e += 2) {
+      f32x2 p;
+      p.x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ch + e], c2, negm));
+      p.y = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ch + e + 1], c2, negm));
+      const f16x2v h = __builtin_convertvector(p, f16x2v);
+      st.lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, h),
+                                       __builtin_bit_cast(fp16x2, ones), st.lsum, false);
+      pf[ch][e] = h.x;
+      pf[ch][e + 1] = h.y;
     }
   }
-
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- O^T[dim][row] += V^T[dim][key] P^T[key][row]. Key slot 8*half + 4*rr + e of chunk ch
-  // is key 16*ch + 4*half + 8*rr + e, in the A operand (transposed read) and in pf[ch].
-  {
-    const char *vt = v_buf<B>();
-    const int g = c.lane & 15;
-    const int m0 = 16 * ((c.lane >> 4) & 1);
-    const char *vbase = vt + (4 * c.half + (g >> 2)) * kVRow + (m0 + 4 * (g & 3)) * 2;
-    auto vfrag = [&](int ch, int d) -> f16x8 {
-      f16x8 vf;
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const fp16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            (lds_fp16x4 *)(vbase + (16 * ch + 8 * rr) * kVRow + 64 * d));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vf[4 * rr + e] = (_Float16)x[e];
-      }
-      return vf;
-    };
-    f16x8 vq[kVPrefetch + 1];
-#pragma unroll
-    for (int it = 0; it < kVPrefetch; ++it) vq[it] = vfrag(it / kDBlocks, it % kDBlocks);
-#pragma unroll
-    for (int it = 0; it < 2 * kDBlocks; ++it) {
-      const int ch = it / kDBlocks, d = it % kDBlocks;
-      if (it + kVPrefetch < 2 * kDBlocks) {
-        const int it2 = it + kVPrefetch;
-        vq[it2 % (kVPrefetch + 1)] = vfrag(it2 / kDBlocks, it2 % kDBlocks);
-      }
-      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[it % (kVPrefetch + 1)], pf[ch], o[d], 0,
-                                                    0, 0);
-      pin_agpr(o[d]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // ---- end of the tile: this thread's loads of tile t+1 (and the slots of t+2) have had the
-  // whole tile to land; convert them to the fp16 latent tile, then publish with the barrier
-  if (have_next) {
-    wait_tile_loads();
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) convert_unit<NB>(c, i, ok_next);
-  }
-  slots_to_sgpr(slot_vec, slots);
-
-  if (have_next && c.lane == 0)
-    reinterpret_cast<uint8_t *>(&g_okbits[NB])[c.wave] = uint8_t(ok_next);
-  __syncthreads();
 }
 
 template <bool kArgmax>
@@ -488,6 +500,7 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   Ctx c;
   c.kv = static_cast<const uint16_t *>(a.kv);
   c.kvi = a.kv_indices + seg.kv0;
+  c.zero = ws.zero_row;
   c.num_slots = a.num_slots;
   c.status = ws.status;
   c.P = seg.P;
@@ -508,15 +521,27 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   c.k1 = min(seg.L, c.k0 + chunk);
   const int ntiles = (c.k1 - c.k0 + kTK - 1) / kTK;
 
-  // ---- prologue: tile 0 loaded and converted, slots of tile 1 fetched
-  WaveSlots slots;
-  uint32_t ok0 = 0;
+  const LaneOffs lo = lane_offsets(c);
+  char *const raw0 = g_lds;
+  char *const raw1 = g_lds + kRawTile;
+  char *const v0 = g_lds + kVOff;
+  char *const v1 = g_lds + kVOff + kVTile;
+
+  // ---- prologue: tiles 0 and 1 requested, the slots of tile 2 fetched, q loaded
   int64_t slot_vec = -1;
   if (ntiles > 0) {
-    slots_to_sgpr(fetch_slots_vec(c, 0), slots);
-    ok0 = wave_ok_bits(c, 0, slots);
-    issue_tile<0>(c, slots, ok0);
-    slot_vec = fetch_slots_vec(c, 1);
+    const int64_t s0 = fetch_slot(c, 0), s1 = fetch_slot(c, 1);
+    const TileLoads t0 = plan_tile(c, 0, s0);
+    const TileLoads t1 = plan_tile(c, 1, s1);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, t0, lds_addr(raw0), i);
+    issue_rope(c, t0, lds_addr(raw0));
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, t1, lds_addr(raw1), i);
+    issue_rope(c, t1, lds_addr(raw1));
+    publish_ok(c, 0, t0.ok);
+    publish_ok(c, 1, t1.ok);
+    slot_vec = fetch_slot(c, 2);
   }
 
   // query fragments (B operand): row `col`, dims 16*kc + 8*half .. +8
@@ -551,22 +576,58 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   const uint8_t *mseg = a.mask + seg.m0;
   const uint32_t moff = uint32_t(tok) * uint32_t(seg.L);
 
+  f16x8 pf[2];
   if (ntiles > 0) {
     wait_tile_loads();
-    slots_to_sgpr(slot_vec, slots);
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) convert_unit<0>(c, i, ok0);
-    if (c.lane == 0) reinterpret_cast<uint8_t *>(&g_okbits[0])[c.wave] = uint8_t(ok0);
-  }
-  __syncthreads();
+    __syncthreads();
+    // QK^T of tile 0 (and its fp16 copy), softmax
+    StepIO io;
+    io.kraw = raw0;
+    io.vrd = v0;
+    io.vwr = v0;
+    io.dma_raw = 0;
+    TileLoads none;
+    none.addr = 0;
+    none.ok = 0;
+    {
+      f32x16 sacc;
+      matrix_step<true, false, false>(c, lo, io, none, qf, o, sacc, pf);
+      softmax_tile<kArgmax>(c, c.k0, g_okbits[0], sacc, o, st, c2, row_ok, mseg, moff, pf);
+    }
+    __syncthreads();
 
-  for (int t = 0; t < ntiles; t += 2) {
-    tile_step<0, kArgmax>(c, t, ntiles, slots, qf, o, st, c2, row_ok, mseg, moff);
-    if (t + 1 < ntiles)
-      tile_step<1, kArgmax>(c, t + 1, ntiles, slots, qf, o, st, c2, row_ok, mseg, moff);
+    // steady state: step t multiplies P(t) V(t), computes S(t+1) and its softmax, converts
+    // tile t+1 to fp16 and loads tile t+2 (zero rows once past the split)
+    for (int t = 0; t + 1 < ntiles; ++t) {
+      const int b = t & 1;
+      const TileLoads tl = plan_tile(c, t + 2, slot_vec);
+      StepIO sio;
+      sio.kraw = b ? raw0 : raw1;
+      sio.vrd = b ? v1 : v0;
+      sio.vwr = b ? v0 : v1;
+      sio.dma_raw = lds_addr(b ? raw1 : raw0);
+      publish_ok(c, b, tl.ok);
+      slot_vec = fetch_slot(c, t + 3);
+      f32x16 sacc;
+      matrix_step<true, true, true>(c, lo, sio, tl, qf, o, sacc, pf);
+      softmax_tile<kArgmax>(c, c.k0 + (t + 1) * kTK, g_okbits[b ^ 1], sacc, o, st, c2, row_ok,
+                            mseg, moff, pf);
+      wait_tile_loads();
+      __syncthreads();
+    }
+
+    // P V of the last tile
+    StepIO eio;
+    eio.kraw = raw0;
+    eio.vrd = ((ntiles - 1) & 1) ? v1 : v0;
+    eio.vwr = v0;
+    eio.dma_raw = 0;
+    f32x16 unused;
+    matrix_step<false, true, false>(c, lo, eio, none, qf, o, unused, pf);
   }
 
   // ---- write the partial of this split
+  matrix_drain();
   const float ltot = st.lsum + swap_halves(st.lsum);
   if (!row_ok) return;
   const int64_t prow = int64_t(s) * ws.rows_cap + grow;
