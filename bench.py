@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -48,22 +49,46 @@ def algorithmic_work(w, out_bytes=4):
     return by, fl
 
 
+def counter_traffic(kernel_file_stem, workload, sources):
+    """HBM bytes per dispatch from the committed rocprofv3 byte-counter summary of this kernel
+    and workload, or None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_file_stem}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    traffic = digest = None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("traffic per dispatch:"):
+            traffic = int(line.split(":")[1].split()[0])
+        elif line.startswith("kernel sources sha256"):
+            digest = line.rsplit(":", 1)[1].strip()
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, "mla_tree_verify_paged_amd", "csrc", f), "rb").read())
+    return traffic if digest == h.hexdigest() else None
+
+
 class HipEvents:
     """hipEvent_t handles from the HIP runtime torch uses (same process-wide copy)."""
 
     def __init__(self):
         import torch  # noqa: F401  (loads the runtime)
         self.rt = ctypes.CDLL("libamdhip64.so.7")
-        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                    ctypes.c_uint]
         self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                 ctypes.c_void_p]
         self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
+    # timing-only events: no system-scope fence when recorded (its cache writeback would be
+    # charged to the kernel being timed); the host synchronises the device before reading them
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def create(self):
         e = ctypes.c_void_p()
-        rc = self.rt.hipEventCreate(ctypes.byref(e))
+        rc = self.rt.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
-            raise RuntimeError(f"hipEventCreate failed: {rc}")
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
         return e.value
 
     def elapsed_ms(self, a, b):
@@ -113,8 +138,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 256 MiB device-to-device copy (for scaling "
-                         "hardware byte counters)")
+                    help="also run one elementwise kernel that reads and writes 256 MiB (for "
+                         "scaling hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -216,14 +241,18 @@ def main():
     log(f"graph warm {graph_us:.2f} us/step; cold median {np.median(cold):.2f} us")
 
     if args.copy_calibration:
-        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+        # one elementwise kernel that reads 256 MiB and writes 256 MiB (fp32 x 1.0): the
+        # reference for scaling the hardware byte counters of the kernels above
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
     by, fl = algorithmic_work(w)
+    traffic = (counter_traffic("mfma_partial_kernel", w.name, ["verify_mfma.hip", "va_internal.h"])
+               if kernel_name == "mfma" else None)
     part_s = part_ms.mean() * 1e-3
     us = ms_per_step * 1e3
     achieved = fl / part_s / 1e12
@@ -265,7 +294,7 @@ def main():
             "peak": PEAK_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "kernel": f"{kernel_name} partial (split-K)",
         },
         "cpu_baseline": None,
