@@ -8,12 +8,12 @@
 // and the argmax is the argmax of the split holding the largest max score (lowest split,
 // hence lowest key position, on ties).
 //
-// One wavefront per row. The per-split scalars are read lane-parallel (lane s holds split s);
-// the 2 KB partial rows of the splits with nonzero weight are then streamed with up to eight
-// splits in flight, lane l owning output dims [8l, 8l+8). The combine also owns output
-// validation: a row whose token belongs to no valid request is written empty (out 0,
-// lse -inf, argmax -1) and the matching status bit is set, so every output element is
-// defined whatever the device-side tables hold.
+// Two wavefronts per row, each lane owning 4 output dims: the per-split scalars are read
+// lane-parallel (lane s holds split s), then the 16-byte slices of up to 32 splits with
+// nonzero weight are loaded at once, so the partial rows of every split are in flight
+// together. The combine also owns output validation: a row whose token belongs to no valid
+// request is written empty (out 0, lse -inf, argmax -1) and the matching status bit is set,
+// so every output element is defined whatever the device-side tables hold.
 #include <math.h>
 
 #include "va_internal.h"
@@ -22,8 +22,9 @@ namespace va {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / 64;
-constexpr int kBatch = 8;  // splits whose partial rows are in flight at once
+constexpr int kThreadsPerRow = 128;                     // 4 dims each
+constexpr int kRowsPerBlock = kThreads / kThreadsPerRow;
+constexpr int kBatch = 32;                              // splits whose slices are in flight
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -42,26 +43,42 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ void store_row(const RunArgs &a, int64_t row, int lane, const float v[8]) {
+// the 4 output dims [dim0, dim0 + 4) of `row`
+__device__ void store4(const RunArgs &a, int64_t row, int dim0, const float4 &v) {
   if (a.out_bf16) {
-    uint4 w;
-    w.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-    w.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-    w.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
-    w.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
-    reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + row * kLatent)[lane] = w;
+    uint2 w;
+    w.x = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
+    w.y = f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16);
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + row * kLatent + dim0) = w;
   } else {
-    float4 *dst = reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * kLatent);
-    dst[2 * lane] = make_float4(v[0], v[1], v[2], v[3]);
-    dst[2 * lane + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + row * kLatent + dim0) = v;
   }
 }
 
 __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace ws) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
+  const int sub = threadIdx.x % kThreadsPerRow;            // 0..127 within the row
+  const bool lead = sub == 0;                              // writes the row's scalars
+  const int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
   if (row >= a.num_tokens * a.H) return;
   const int64_t t = row / a.H;
+  const int dim0 = 4 * sub;
+  const int S = ws.splits;
+  const int64_t stride = ws.rows_cap;
+  const float *plse = ws.part_lse + row;
+  const float *pmax = ws.part_max + row;
+
+  // Requested before the row is validated, so that one memory round trip serves all of them:
+  // the slices of the first kBatch splits and the scalars of the first 64. Every address is
+  // inside the workspace (row < num_tokens * H <= rows_cap); an invalid row discards them.
+  float4 x[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k)
+    x[k] = k < S ? *reinterpret_cast<const float4 *>(ws.part_o + (int64_t(k) * stride + row) *
+                                                                     kLatent + dim0)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float lse0 = lane < S ? plse[lane * stride] : -INFINITY;
+  const float max0 = lane < S ? pmax[lane * stride] : -INFINITY;
 
   // the request that owns token t: the last r with qo_indptr[r] <= t
   int lo = 0, hi = a.bs;  // answer in [lo, hi)
@@ -80,27 +97,20 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
     bad = 8u;
   }
 
-  float v[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) v[c] = 0.f;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (!ok) {
-    if (lane == 0) {
+    if (lead) {
       atomicOr(ws.status, bad);
       if (a.out_lse) a.out_lse[row] = -INFINITY;
       if (a.out_argmax) a.out_argmax[row] = -1;
     }
-    store_row(a, row, lane, v);
+    store4(a, row, dim0, v);
     return;
   }
 
-  const int S = ws.splits;
-  const float *plse = ws.part_lse + row;
-  const float *pmax = ws.part_max + row;
-  const int64_t stride = ws.rows_cap;
-
-  // per-split scalars, lane-parallel
-  float M = -INFINITY, best = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += 64) {
+  // per-split scalars, lane-parallel (lane s holds split s, then s + 64, ...)
+  float M = lse0, best = max0;
+  for (int s0 = 64; s0 < S; s0 += 64) {
     const int s = s0 + lane;
     if (s < S) {
       M = fmaxf(M, plse[s * stride]);
@@ -113,59 +123,45 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   float W = 0.f;
   int arg = -1;
   if (M != -INFINITY) {
-    for (int s0 = 0; s0 < S; s0 += 64) {
+    for (int s0 = 0; s0 < S; s0 += kBatch) {
+      // lane j < kBatch: the weight of split s0 + j
       const int s = s0 + lane;
-      const float ls = s < S ? plse[s * stride] : -INFINITY;
-      const float w = ls == -INFINITY ? 0.f : expf(ls - M);
-      W += wave_sum(w);
-      if (arg < 0) {
-        const uint64_t hit = __ballot(s < S && pmax[s * stride] == best);
+      // splits below 64 come from lane s of the speculative read, the rest from memory
+      const float lsh = __shfl(lse0, s & 63, 64);
+      float ls = -INFINITY;
+      if (lane < kBatch && s < S) ls = s < 64 ? lsh : plse[s * stride];
+      const float wgt = ls == -INFINITY ? 0.f : expf(ls - M);
+      W += wave_sum(wgt);
+      if (arg < 0) {  // wave-uniform
+        const uint64_t hit = __ballot(lane < kBatch && s < S && pmax[s * stride] == best);
         if (hit) arg = ws.part_arg[(s0 + __builtin_ctzll(hit)) * stride + row];
       }
-      uint64_t live = __ballot(w != 0.f);
-      while (live) {
-        // up to kBatch splits with nonzero weight: issue their loads, then accumulate
-        int idx[kBatch];
-        float wt[kBatch];
+      const uint32_t live = uint32_t(__ballot(wgt != 0.f));
+      if (s0 > 0) {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-          idx[k] = -1;
-          wt[k] = 0.f;
-          if (live) {
-            const int j = __builtin_ctzll(live);
-            live &= live - 1;
-            idx[k] = s0 + j;
-            wt[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
-          }
+          if ((live >> k) & 1u)
+            x[k] = *reinterpret_cast<const float4 *>(
+                ws.part_o + (int64_t(s0 + k) * stride + row) * kLatent + dim0);
+          else
+            x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        float4 x0[kBatch], x1[kBatch];
+      }
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          if (idx[k] >= 0) {
-            const float4 *src = reinterpret_cast<const float4 *>(
-                ws.part_o + (int64_t(idx[k]) * stride + row) * kLatent);
-            x0[k] = src[2 * lane];
-            x1[k] = src[2 * lane + 1];
-          } else {
-            x0[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            x1[k] = x0[k];
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          v[0] = fmaf(wt[k], x0[k].x, v[0]); v[1] = fmaf(wt[k], x0[k].y, v[1]);
-          v[2] = fmaf(wt[k], x0[k].z, v[2]); v[3] = fmaf(wt[k], x0[k].w, v[3]);
-          v[4] = fmaf(wt[k], x1[k].x, v[4]); v[5] = fmaf(wt[k], x1[k].y, v[5]);
-          v[6] = fmaf(wt[k], x1[k].z, v[6]); v[7] = fmaf(wt[k], x1[k].w, v[7]);
+      for (int k = 0; k < kBatch; ++k) {
+        // a split with zero weight contributes nothing (its slice is not read, or is zero)
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
+        if ((live >> k) & 1u) {
+          v.x = fmaf(wk, x[k].x, v.x); v.y = fmaf(wk, x[k].y, v.y);
+          v.z = fmaf(wk, x[k].z, v.z); v.w = fmaf(wk, x[k].w, v.w);
         }
       }
     }
     const float inv = 1.f / W;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] *= inv;
+    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
   }
-  store_row(a, row, lane, v);
-  if (lane == 0) {
+  store4(a, row, dim0, v);
+  if (lead) {
     if (a.out_lse) a.out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
     if (a.out_argmax) a.out_argmax[row] = arg;
   }

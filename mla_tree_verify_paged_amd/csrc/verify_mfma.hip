@@ -70,7 +70,7 @@ constexpr int kQFrags = kDim / 16;          // 36 bf16x8 B-operand fragments per
 constexpr int kLatFrags = kLatent / 16;     // the first 32 of them are latent dims
 constexpr int kDBlocks = kLatent / 32;      // 16 output dim blocks of 32
 constexpr int kNumPV = 2 * kDBlocks;        // 32 P.V products per tile
-constexpr int kDepth = 6;                   // operand fragment reads in flight
+constexpr int kDepth = 3;                   // operand fragment reads in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.0f;            // lazy-rescale threshold (log2 units)
@@ -174,6 +174,12 @@ __device__ __forceinline__ void dma_lanes(const void *src, uint32_t lds) {
 __device__ __forceinline__ void wait_tile_loads() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
+// The same, but leaving up to 9 loads in flight: the prologue issues the 9 loads of tile 1
+// after those of tile 0 (always; the slot fetch after them is skipped when no lane needs it),
+// and vector-memory loads complete in issue order, so tile 0 and q have landed.
+__device__ __forceinline__ void wait_loads_but_tile1() {
+  asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+}
 
 // Per-workgroup constants of one split.
 struct Ctx {
@@ -267,20 +273,67 @@ struct RowState {
   int best_j;   // argmax key position
 };
 
-// ---- the matrix phase of one pipeline step
-// Operation p of the step: with both products, QK_0 PV_0 QK_1 PV_1 ... QK_31 PV_31 QK_32..35;
-// otherwise the one product's operations in order.
-template <bool QK, bool PV> struct Sched {
-  static constexpr int kOps = (QK ? kQFrags : 0) + (PV ? kNumPV : 0);
-  static constexpr bool is_pv(int p) { return QK && PV ? (p < 2 * kNumPV && (p & 1)) : PV; }
-  static constexpr int index(int p) {
-    return QK && PV ? (p < 2 * kNumPV ? (p >> 1) : p - kNumPV) : p;
+// ---- one pipeline step
+//
+// A step issues the 68 matrix instructions of one tile's worth of work in a fixed order
+// (written as a table), and slots the vector work between them:
+//  kFirst - QK^T of tile 0 (36 instructions) and the fp16 copy of tile 0;
+//  kMain  - phase A: exp/round/sum of P(t) interleaved with QK^T fragments 0..11 of tile t+1;
+//           phase B: P(t).V(t) interleaved with QK^T fragments 12..35 of tile t+1, the fp16
+//           copy of tile t+1, the loads of tile t+2 and the slot fetch of tile t+3; the last
+//           eight P.V products cover the latency of the final QK^T result and the merge of
+//           the two score chains;
+//  kLast  - exp/round/sum of P(t), then P(t).V(t).
+// QK^T fragments alternate between two accumulation chains (even and odd fragments), so a
+// matrix instruction never waits on the one just before it.
+enum StepKind { kFirst = 0, kMain = 1, kLast = 2 };
+
+struct Op {
+  int8_t pv;    // 1: P.V product, 0: QK^T fragment
+  int8_t idx;   // fragment index (QK^T: 0..35; P.V: 0..31, chunk = idx / 16, dim block = idx % 16)
+};
+template <int N> struct OpTable { Op op[N]; };
+
+constexpr int kPhaseA = 12;  // QK^T fragments in phase A of a main step
+
+template <int K> struct StepPlan;
+template <> struct StepPlan<kFirst> {
+  static constexpr int kOps = kQFrags;
+  static constexpr OpTable<kOps> table() {
+    OpTable<kOps> t{};
+    for (int i = 0; i < kOps; ++i) t.op[i] = Op{0, int8_t(i)};
+    return t;
   }
-  // conversion unit u: read after operation rd(u), converted and written after wr(u)
-  static constexpr int wr(int u) {
-    return QK && PV ? (u < 4 ? 49 + 4 * u : 60 + u) : 6 + 4 * u;
+  // conversion unit u: read after op rd(u), one pair converted after each of the next four
+  // ops, written after op rd(u) + 4
+  static constexpr int rd(int u) { return 2 + 4 * u; }
+};
+template <> struct StepPlan<kMain> {
+  static constexpr int kOps = kQFrags + kNumPV;
+  static constexpr OpTable<kOps> table() {
+    OpTable<kOps> t{};
+    int p = 0;
+    for (int k = 0; k < kPhaseA; ++k) t.op[p++] = Op{0, int8_t(k)};
+    int q = kPhaseA, v = 0;
+    while (q < kQFrags || v < kNumPV) {
+      if (v < kNumPV) t.op[p++] = Op{1, int8_t(v++)};
+      if (q < kQFrags) t.op[p++] = Op{0, int8_t(q++)};
+    }
+    return t;
   }
-  static constexpr int rd(int u) { return wr(u) - 2; }
+  static constexpr int rd(int u) { return kPhaseA + 2 + 6 * u; }
+  static constexpr int kDmaOp = kPhaseA + 1;    // loads of tile t+2 after ops 13..21
+  static constexpr int kSlotOp = kDmaOp + 9;    // slot fetch of tile t+3 after op 22
+  static constexpr int kMergeOp = kOps - 7;     // chain merge after ops 61..67
+};
+template <> struct StepPlan<kLast> {
+  static constexpr int kOps = kNumPV;
+  static constexpr OpTable<kOps> table() {
+    OpTable<kOps> t{};
+    for (int i = 0; i < kOps; ++i) t.op[i] = Op{1, int8_t(i)};
+    return t;
+  }
+  static constexpr int rd(int u) { return -100; }
 };
 
 struct StepIO {
@@ -299,12 +352,36 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-template <bool QK, bool PV, bool kLoads>
-__device__ __forceinline__ void matrix_step(const Ctx &c, const LaneOffs &lo, const StepIO &io,
-                                            const TileLoads &tl, const bf16x8 *qf, f32x16 *o,
-                                            f32x16 &sacc, const f16x8 *pf) {
-  using S = Sched<QK, PV>;
-  constexpr int N = S::kOps;
+// P(t) = exp2(s*c2 - m) rounded to nearest-even fp16 (v_cvt_pk_f16_f32: unbiased, so the
+// denominator summed from the rounded values does not drift), in 8 parts of two keys; the
+// sum uses v_dot2.
+__device__ __forceinline__ void p_part(int part, const f32x16 &s, float c2, float negm,
+                                       float &lsum, f16x8 *pf) {
+  const int ch = part >> 2, e = 2 * (part & 3);
+  f32x2 p;
+  p.x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ch + e], c2, negm));
+  p.y = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ch + e + 1], c2, negm));
+  const f16x2v h = __builtin_convertvector(p, f16x2v);
+  const f16x2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+  lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, h), __builtin_bit_cast(fp16x2, ones),
+                                lsum, false);
+  pf[ch][e] = h.x;
+  pf[ch][e + 1] = h.y;
+}
+
+__device__ __forceinline__ float neg_max(const RowState &st) {
+  return st.m == -INFINITY ? 0.f : -st.m;
+}
+
+template <int K>
+__device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const StepIO &io,
+                                     const TileLoads &tl, int64_t &slot_vec, int slot_tile,
+                                     const bf16x8 *qf, f32x16 *o, f32x16 &snext,
+                                     const f32x16 &scur, RowState &st, float c2, f16x8 *pf) {
+  using Plan = StepPlan<K>;
+  constexpr int N = Plan::kOps;
+  constexpr OpTable<N> T = Plan::table();
+  constexpr bool kQK = K != kLast;
   const char *klat = io.kraw + lo.k_lat;
   const char *krope = io.kraw + lo.k_rope;
   const char *vtr = io.vrd + lo.v_tr;
@@ -313,20 +390,28 @@ __device__ __forceinline__ void matrix_step(const Ctx &c, const LaneOffs &lo, co
 
   u32x4 fr[kDepth + 1];
   u32x4 craw[kRowsPerWave];
+  f32x16 sa, sb;  // the two score chains
+  const float negm = neg_max(st);
+
+  if constexpr (K == kLast) {
+#pragma unroll
+    for (int part = 0; part < 8; ++part) p_part(part, scur, c2, negm, st.lsum, pf);
+  }
 
   // operand fragment of operation p
   auto load = [&](auto pc) __attribute__((always_inline)) {
     constexpr int p = decltype(pc)::value;
     if constexpr (p < N) {
+      constexpr Op op = T.op[p];
       u32x4 r;
-      if constexpr (!S::is_pv(p)) {
-        constexpr int kc = S::index(p);
+      if constexpr (!op.pv) {
+        constexpr int kc = op.idx;
         if constexpr (kc < kLatFrags)
           r = *reinterpret_cast<const u32x4 *>(klat + 32 * kc);
         else
           r = *reinterpret_cast<const u32x4 *>(krope + 256 * (kc - kLatFrags));
       } else {
-        constexpr int it = S::index(p), ch = it / kDBlocks, d = it % kDBlocks;
+        constexpr int it = op.idx, ch = it / kDBlocks, d = it % kDBlocks;
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
           const fp16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
@@ -343,51 +428,69 @@ __device__ __forceinline__ void matrix_step(const Ctx &c, const LaneOffs &lo, co
   static_for<0, kDepth>(load);
   static_for<0, N>([&](auto pc) __attribute__((always_inline)) {
     constexpr int p = decltype(pc)::value;
+    constexpr Op op = T.op[p];
     load(std::integral_constant<int, p + kDepth>{});
     const u32x4 a = fr[p % (kDepth + 1)];
-    if constexpr (S::is_pv(p)) {
-      constexpr int it = S::index(p), ch = it / kDBlocks, d = it % kDBlocks;
+    if constexpr (op.pv) {
+      constexpr int ch = op.idx / kDBlocks, d = op.idx % kDBlocks;
       pv_mfma(o[d], a, pf[ch]);
     } else {
-      constexpr int kc = S::index(p);
+      constexpr int kc = op.idx;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
       if constexpr (kc == 0) {
         const f32x16 zero = {};
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kc],
-                                                       zero, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kc], zero, 0, 0, 0);
+      } else if constexpr (kc == 1) {
+        const f32x16 zero = {};
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kc], zero, 0, 0, 0);
+      } else if constexpr (kc & 1) {
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kc], sb, 0, 0, 0);
       } else {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kc],
-                                                       sacc, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kc], sa, 0, 0, 0);
       }
     }
-    // loads of the tile two steps ahead: 8 latent rows, then the rope block
-    if constexpr (kLoads) {
-      if constexpr (p >= 1 && p <= kRowsPerWave) issue_latent(c, tl, io.dma_raw, p - 1);
-      if constexpr (p == kRowsPerWave + 1) issue_rope(c, tl, io.dma_raw);
+    // phase A: P(t), two keys after each of the first eight fragments
+    if constexpr (K == kMain && p < 8) p_part(p, scur, c2, negm, st.lsum, pf);
+    // the loads of tile t+2 (zero rows past the split), then the slots of tile t+3
+    if constexpr (K == kMain) {
+      constexpr int dp = p - Plan::kDmaOp;
+      if constexpr (dp >= 0 && dp < kRowsPerWave) issue_latent(c, tl, io.dma_raw, dp);
+      if constexpr (dp == kRowsPerWave) issue_rope(c, tl, io.dma_raw);
+      if constexpr (p == Plan::kSlotOp) slot_vec = fetch_slot(c, slot_tile);
     }
     // fp16 copy of the latent units this thread loaded for the tile QK reads
-    if constexpr (QK) {
+    if constexpr (kQK) {
       static_for<0, kRowsPerWave>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
-        if constexpr (p == S::rd(u))
+        constexpr int r0 = Plan::rd(u);
+        if constexpr (p == r0)
           craw[u] = *reinterpret_cast<const u32x4 *>(cvr + kLatStride * u);
-        if constexpr (p == S::wr(u)) {
-          u32x4 h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = bf16pair_to_f16pair(craw[u][e]);
-          *reinterpret_cast<u32x4 *>(cvw + kVRow * u) = h;
-        }
+        if constexpr (p > r0 && p <= r0 + 4) craw[u][p - r0 - 1] =
+            bf16pair_to_f16pair(craw[u][p - r0 - 1]);
+        if constexpr (p == r0 + 4) *reinterpret_cast<u32x4 *>(cvw + kVRow * u) = craw[u];
       });
+    }
+    // merge of the two score chains
+    if constexpr (K == kMain) {
+      constexpr int mp = p - Plan::kMergeOp;
+      if constexpr (mp >= 0) {
+#pragma unroll
+        for (int e = (16 * mp) / 7; e < (16 * (mp + 1)) / 7; ++e) snext[e] = sa[e] + sb[e];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   });
+  if constexpr (K == kFirst) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) snext[e] = sa[e] + sb[e];
+  }
 }
 
-// ---- softmax of one tile's scores (sacc): mask, max, lazy rescale, P = exp2 rounded to fp16
+// ---- the rest of the softmax of one tile's scores: mask, max (and argmax), lazy rescale
 template <bool kArgmax>
-__device__ __forceinline__ void softmax_tile(const Ctx &c, int kb, uint32_t okbits,
-                                             f32x16 &sacc, f32x16 *o, RowState &st, float c2,
-                                             bool row_ok, const uint8_t *mseg, uint32_t moff,
-                                             f16x8 *pf) {
+__device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits, f32x16 &sacc,
+                                          f32x16 *o, RowState &st, float c2, bool row_ok,
+                                          const uint8_t *mseg, uint32_t moff) {
   // raw scores; invisible keys -> -inf. Accumulator e holds key kb + 8*(e/4) + 4*half + e%4
   // of row `col`. Masking is skipped for tiles of usable prefix keys only.
   const bool tail = kb + kTK > c.P;
@@ -452,25 +555,6 @@ __device__ __forceinline__ void softmax_tile(const Ctx &c, int kb, uint32_t okbi
     for (int d = 0; d < kDBlocks; ++d) scale_acc(o[d], alpha);
     matrix_drain();
   }
-  const float negm = st.m == -INFINITY ? 0.f : -st.m;
-
-  // P = exp2(s*c2 - m) rounded to nearest-even fp16 (v_cvt_pk_f16_f32: unbiased, so the
-  // denominator summed from the rounded values does not drift); the sum uses v_dot2
-  const f16x2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-  for (int ch = 0; ch < 2; ++ch) {
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      f32x2 p;
-      p.x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ch + e], c2, negm));
-      p.y = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * ch + e + 1], c2, negm));
-      const f16x2v h = __builtin_convertvector(p, f16x2v);
-      st.lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, h),
-                                       __builtin_bit_cast(fp16x2, ones), st.lsum, false);
-      pf[ch][e] = h.x;
-      pf[ch][e + 1] = h.y;
-    }
-  }
 }
 
 template <bool kArgmax>
@@ -527,10 +611,26 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   char *const v0 = g_lds + kVOff;
   char *const v1 = g_lds + kVOff + kVTile;
 
-  // ---- prologue: tiles 0 and 1 requested, the slots of tile 2 fetched, q loaded
+  // ---- prologue: the slots of tiles 0 and 1 and the query rows are requested together; the
+  // tile loads follow as soon as the slots arrive (loads complete in order, so that wait
+  // does not wait for q); the slots of tile 2 are fetched last
+  int64_t s0 = -1, s1 = -1;
+  if (ntiles > 0) {
+    s0 = fetch_slot(c, 0);
+    s1 = fetch_slot(c, 1);
+  }
+  // query fragments (B operand): row `col`, dims 16*kc + 8*half .. +8; all requested now,
+  // made opaque to the optimiser only after the tile loads are issued (below)
+  u32x4 qv[kQFrags];
+  {
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(
+        static_cast<const uint16_t *>(a.q) + grow * kDim);
+#pragma unroll
+    for (int kc = 0; kc < kQFrags; ++kc)
+      qv[kc] = __builtin_bit_cast(u32x4, qrow[2 * kc + c.half]);
+  }
   int64_t slot_vec = -1;
   if (ntiles > 0) {
-    const int64_t s0 = fetch_slot(c, 0), s1 = fetch_slot(c, 1);
     const TileLoads t0 = plan_tile(c, 0, s0);
     const TileLoads t1 = plan_tile(c, 1, s1);
 #pragma unroll
@@ -543,19 +643,13 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
     publish_ok(c, 1, t1.ok);
     slot_vec = fetch_slot(c, 2);
   }
-
-  // query fragments (B operand): row `col`, dims 16*kc + 8*half .. +8
+  // keep the query fragments resident: without this the compiler re-reads q inside the tile
+  // loop. (Placed after every load is issued: it makes the wave wait for q.)
   bf16x8 qf[kQFrags];
-  {
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(
-        static_cast<const uint16_t *>(a.q) + grow * kDim);
 #pragma unroll
-    for (int kc = 0; kc < kQFrags; ++kc) {
-      u32x4 v = __builtin_bit_cast(u32x4, qrow[2 * kc + c.half]);
-      // keep the fragment resident: without this the compiler re-reads q inside the tile loop
-      asm volatile("" : "+v"(v));
-      qf[kc] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int kc = 0; kc < kQFrags; ++kc) {
+    asm volatile("" : "+v"(qv[kc]));
+    qf[kc] = __builtin_bit_cast(bf16x8, qv[kc]);
   }
 
   f32x16 o[kDBlocks];
@@ -578,26 +672,31 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
 
   f16x8 pf[2];
   if (ntiles > 0) {
-    wait_tile_loads();
+    // q and tile 0 have landed once at most the 9 loads of tile 1 are outstanding; tile 1 is
+    // waited for before the barrier that ends step 0
+    wait_loads_but_tile1();
     __syncthreads();
-    // QK^T of tile 0 (and its fp16 copy), softmax
-    StepIO io;
-    io.kraw = raw0;
-    io.vrd = v0;
-    io.vwr = v0;
-    io.dma_raw = 0;
     TileLoads none;
     none.addr = 0;
     none.ok = 0;
+    // S(0) and the fp16 copy of tile 0, its max
+    f32x16 scur;
     {
-      f32x16 sacc;
-      matrix_step<true, false, false>(c, lo, io, none, qf, o, sacc, pf);
-      softmax_tile<kArgmax>(c, c.k0, g_okbits[0], sacc, o, st, c2, row_ok, mseg, moff, pf);
+      StepIO io;
+      io.kraw = raw0;
+      io.vrd = v0;
+      io.vwr = v0;
+      io.dma_raw = 0;
+      const f32x16 unused = {};
+      step<kFirst>(c, lo, io, none, slot_vec, 0, qf, o, scur, unused, st, c2, pf);
+      score_max<kArgmax>(c, c.k0, g_okbits[0], scur, o, st, c2, row_ok, mseg, moff);
     }
+    wait_tile_loads();
     __syncthreads();
 
-    // steady state: step t multiplies P(t) V(t), computes S(t+1) and its softmax, converts
-    // tile t+1 to fp16 and loads tile t+2 (zero rows once past the split)
+    // steady state: step t finishes the softmax of tile t and multiplies P(t) V(t), computes
+    // S(t+1) and its max, converts tile t+1 to fp16 and loads tile t+2 (zero rows once past
+    // the split)
     for (int t = 0; t + 1 < ntiles; ++t) {
       const int b = t & 1;
       const TileLoads tl = plan_tile(c, t + 2, slot_vec);
@@ -607,23 +706,23 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
       sio.vwr = b ? v0 : v1;
       sio.dma_raw = lds_addr(b ? raw1 : raw0);
       publish_ok(c, b, tl.ok);
-      slot_vec = fetch_slot(c, t + 3);
-      f32x16 sacc;
-      matrix_step<true, true, true>(c, lo, sio, tl, qf, o, sacc, pf);
-      softmax_tile<kArgmax>(c, c.k0 + (t + 1) * kTK, g_okbits[b ^ 1], sacc, o, st, c2, row_ok,
-                            mseg, moff, pf);
+      f32x16 snext;
+      step<kMain>(c, lo, sio, tl, slot_vec, t + 3, qf, o, snext, scur, st, c2, pf);
+      score_max<kArgmax>(c, c.k0 + (t + 1) * kTK, g_okbits[b ^ 1], snext, o, st, c2, row_ok,
+                         mseg, moff);
+      scur = snext;
       wait_tile_loads();
       __syncthreads();
     }
 
-    // P V of the last tile
+    // P(t) V(t) of the last tile
     StepIO eio;
     eio.kraw = raw0;
     eio.vrd = ((ntiles - 1) & 1) ? v1 : v0;
     eio.vwr = v0;
     eio.dma_raw = 0;
-    f32x16 unused;
-    matrix_step<false, true, false>(c, lo, eio, none, qf, o, unused, pf);
+    f32x16 unused2;
+    step<kLast>(c, lo, eio, none, slot_vec, 0, qf, o, unused2, scur, st, c2, pf);
   }
 
   // ---- write the partial of this split
