@@ -135,6 +135,9 @@ def main():
                     choices=["tiny", "short", "long", "segmented", "stress"])
     ap.add_argument("--kernel", default="auto", choices=["auto", "simple", "mfma"])
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--layout", default="combined", choices=["combined", "split"],
+                    help="key slots: tree slots at the tail of each kv_indices segment, or "
+                         "prefix-only kv_indices plus out_cache_loc")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -168,10 +171,18 @@ def main():
     lse = torch.empty((w.num_tokens, w.num_heads), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
+    split = args.layout == "split"
+    kvi = dev["kv_indices_prefix"] if split else dev["kv_indices"]
+    kvp = dev["kv_indptr_prefix"] if split else dev["kv_indptr"]
+    ocl = dev["out_cache_loc"] if split else None
+
+    def run_on(stream_handle):
+        va.run(dev["q"], dev["kv_buffer"], kvi, kvp, dev["qo_indptr"], dev["custom_mask"],
+               dev["mask_indptr"], w.scale, out, lse, None, bs=w.bs, num_tokens=w.num_tokens,
+               stream=stream_handle, out_cache_loc=ocl)
+
     def step():
-        va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"],
-               dev["qo_indptr"], dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse,
-               None, bs=w.bs, num_tokens=w.num_tokens, stream=stream.cuda_stream)
+        run_on(stream.cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -206,17 +217,11 @@ def main():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        step_stream = s.cuda_stream
-        va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"],
-               dev["qo_indptr"], dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse,
-               None, bs=w.bs, num_tokens=w.num_tokens, stream=step_stream)
+        run_on(s.cuda_stream)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"],
-               dev["qo_indptr"], dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse,
-               None, bs=w.bs, num_tokens=w.num_tokens,
-               stream=torch.cuda.current_stream().cuda_stream)
+        run_on(torch.cuda.current_stream().cuda_stream)
     for _ in range(5):
         g.replay()
     torch.cuda.synchronize()
@@ -275,6 +280,7 @@ def main():
                         f"[num_tok,H,576] and paged latent KV [{w.num_slots},576]",
             "kernel": kernel_name,
             "num_splits": int(info.num_splits),
+            "slot_layout": args.layout,
             "out_dtype": "fp32",
         },
         "effective_GBps": round(by / (us * 1e-6) / 1e9, 2),

@@ -24,10 +24,17 @@
  *     sections "The Investigation", "The Three-Edits Sequence", "Why the C-ABI Edit Matters"
  *     and "Assumptions and Design Decisions".
  *
- * Per request r (T_r = qo_indptr[r+1]-qo_indptr[r] tree tokens, L_r = kv_indptr[r+1]-
- * kv_indptr[r] keys, P_r = L_r - T_r prefix keys), tree token i, head h:
- *   key j (0 <= j < L_r) lives in slot kv_indices[kv_indptr[r] + j]; the last T_r keys are
- *   the tree tokens in query order; key j is visible iff j < P_r or
+ * Per request r with T_r = qo_indptr[r+1]-qo_indptr[r] tree tokens, tree token i, head h.
+ * The key slots come in one of two layouts:
+ *   - out_cache_loc == NULL: L_r = kv_indptr[r+1]-kv_indptr[r] keys, P_r = L_r - T_r, key j
+ *     (0 <= j < L_r) in slot kv_indices[kv_indptr[r] + j]; the last T_r keys are the tree
+ *     tokens in query order;
+ *   - out_cache_loc != NULL: kv_indices[kv_indptr[r] ..] holds the P_r = kv_indptr[r+1]-
+ *     kv_indptr[r] prefix slots only and tree key P_r + k is in slot
+ *     out_cache_loc[qo_indptr[r] + k]; L_r = P_r + T_r. (Prefix slots from kv_indices, new
+ *     tokens' slots from out_cache_loc, told apart by the kv_indptr offsets: "The Final
+ *     Solder Joint", section "The Three-Edits Sequence".)
+ *   key j is visible iff j < P_r or
  *   custom_mask[mask_indptr[r] + i*L_r + j] != 0 (prefix columns are never read);
  *   s_j = sm_scale * <q[t,h,0:576], kv[slot_j,0:576]>,  t = qo_indptr[r] + i;
  *   out[t,h,0:512] = sum_j softmax(s)_j * kv[slot_j, 0:512] over the visible keys;
@@ -124,12 +131,13 @@ va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **ou
  * Enqueues one verify step on `stream`.
  *   q            [num_tokens, H, 576] in_dtype, contiguous.
  *   kv_buffer    [num_slots, 576] in_dtype, contiguous rows (the paged latent cache).
- *   kv_indices   int64 [num_kv_indices]: per request P_r prefix slots then T_r tree slots.
+ *   kv_indices   int64 [num_kv_indices]: per request its L_r slots (prefix, then the tree
+ *                tokens), or only its P_r prefix slots when out_cache_loc is given.
  *   kv_indptr    int32 [bs+1], non-decreasing, kv_indptr[bs] <= num_kv_indices.
  *   qo_indptr    int64 [bs+1], non-decreasing, qo_indptr[bs] == num_tokens.
  *   custom_mask  uint8 [mask_len]: request r's [T_r, L_r] row-major matrix at mask_indptr[r].
  *   mask_indptr  int64 [bs+1] element offsets into custom_mask.
- *   out_cache_loc must be NULL (tree slots come from the tail of each kv_indices segment).
+ *   out_cache_loc NULL, or int64 [num_tokens]: the slot of every tree token (see above).
  *   out          [num_tokens, H, 512] out_dtype.
  *   out_lse      nullable float [num_tokens, H].
  *   out_argmax   nullable int32 [num_tokens, H].

@@ -174,7 +174,8 @@ class VerifyAttn:
         self.out_dtype = out_dtype
 
     def run(self, q, kv_buffer, kv_indices, kv_indptr, qo_indptr, custom_mask, mask_indptr,
-            sm_scale, out, out_lse=None, out_argmax=None, bs=None, num_tokens=None, stream=None):
+            sm_scale, out, out_lse=None, out_argmax=None, bs=None, num_tokens=None, stream=None,
+            out_cache_loc=None):
         import torch
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
@@ -184,7 +185,8 @@ class VerifyAttn:
             num_tokens = q.shape[0]
         verify_attn_run(self.ctx, _ptr(q), _ptr(kv_buffer), kv_buffer.shape[0], _ptr(kv_indices),
                         kv_indices.numel(), _ptr(kv_indptr), _ptr(qo_indptr), _ptr(custom_mask),
-                        custom_mask.numel(), _ptr(mask_indptr), None, int(bs), int(num_tokens),
+                        custom_mask.numel(), _ptr(mask_indptr), _ptr(out_cache_loc), int(bs),
+                        int(num_tokens),
                         float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(out_argmax), stream)
         return out
 

@@ -190,9 +190,6 @@ va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_bu
                           int64_t num_tokens, float sm_scale, void *out, float *out_lse,
                           int32_t *out_argmax, void *stream) {
   if (!ctx) return fail(VA_ERR_NULL, "ctx is NULL");
-  if (out_cache_loc)
-    return fail(VA_ERR_UNSUPPORTED, "out_cache_loc is not supported: pass NULL and keep the "
-                                    "tree slots at the tail of each kv_indices segment");
   if (bs < 0 || bs > ctx->cfg.max_batch)
     return fail(VA_ERR_INVALID, "bs %d out of range [0, %d]", bs, ctx->cfg.max_batch);
   if (num_tokens < 0 || num_tokens > ctx->cfg.max_q_tokens)
@@ -217,6 +214,7 @@ va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_bu
   a.num_slots = num_slots;
   a.kv_indices = kv_indices;
   a.num_kv_indices = num_kv_indices;
+  a.out_cache_loc = out_cache_loc;
   a.kv_indptr = kv_indptr;
   a.qo_indptr = qo_indptr;
   a.mask = custom_mask;

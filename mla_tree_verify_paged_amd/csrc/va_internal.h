@@ -40,6 +40,7 @@ struct RunArgs {
   int64_t num_slots;
   const int64_t *kv_indices;
   int64_t num_kv_indices;
+  const int64_t *out_cache_loc;  // NULL: tree slots end each kv_indices segment
   const int32_t *kv_indptr;
   const int64_t *qo_indptr;
   const uint8_t *mask;
@@ -84,6 +85,9 @@ struct Segment {
   int32_t P;      // prefix keys
   int64_t kv0;    // first kv_indices entry
   int64_t m0;     // first mask byte
+  // the slots of the tree keys (key P + k in slot tree[k]) when they come from
+  // out_cache_loc, else NULL (they are kv_indices[kv0 + P + k])
+  const int64_t *tree;
 };
 
 __device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segment &s) {
@@ -93,9 +97,12 @@ __device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segmen
   s.q0 = q0;
   s.kv0 = k0;
   s.m0 = m0;
-  const int64_t T = q1 - q0, L = k1 - k0;
+  s.tree = nullptr;
+  const int64_t T = q1 - q0, n = k1 - k0;
+  // the split layout: kv_indices holds the prefix, out_cache_loc[q0 .. q1) the tree slots
+  const int64_t L = a.out_cache_loc ? n + T : n;
   s.T = 0; s.L = 0; s.P = 0;
-  if (T < 0 || L < 0 || q0 < 0 || q1 > a.num_tokens || k0 < 0 || k1 > a.num_kv_indices ||
+  if (T < 0 || n < 0 || q0 < 0 || q1 > a.num_tokens || k0 < 0 || k1 > a.num_kv_indices ||
       L < T || L > INT32_MAX || m0 < 0 || (T > 0 && m0 + T * L > a.mask_len) ||
       T * L > INT32_MAX)
     return 2u;  // VA_DEV_SEGMENT (a request's mask segment must stay under 2 GiB)
@@ -103,7 +110,13 @@ __device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segmen
   s.T = int32_t(T);
   s.L = int32_t(L);
   s.P = int32_t(L - T);
+  if (a.out_cache_loc) s.tree = a.out_cache_loc + q0;
   return 0u;
+}
+
+// Slot of key position j (0 <= j < L) of a validated segment.
+__device__ __forceinline__ int64_t segment_slot(const RunArgs &a, const Segment &s, int j) {
+  return (s.tree && j >= s.P) ? s.tree[j - s.P] : a.kv_indices[s.kv0 + j];
 }
 
 // Launchers (each defined next to its kernels).

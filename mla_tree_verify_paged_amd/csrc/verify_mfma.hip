@@ -185,6 +185,7 @@ __device__ __forceinline__ void wait_loads_but_tile1() {
 struct Ctx {
   const uint16_t *kv;
   const int64_t *kvi;   // kv_indices of the request
+  const int64_t *tree;  // the tree keys' slots when they come from out_cache_loc, else NULL
   const uint16_t *zero; // a row of zeros
   int64_t num_slots;
   uint32_t *status;
@@ -198,7 +199,7 @@ struct Ctx {
 __device__ __forceinline__ int64_t fetch_slot(const Ctx &c, int t) {
   int64_t v = -1;
   const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane & 7);
-  if (j < c.k1) v = c.kvi[j];
+  if (j < c.k1) v = (c.tree && j >= c.P) ? c.tree[j - c.P] : c.kvi[j];
   return v;
 }
 
@@ -584,6 +585,7 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   Ctx c;
   c.kv = static_cast<const uint16_t *>(a.kv);
   c.kvi = a.kv_indices + seg.kv0;
+  c.tree = seg.tree;
   c.zero = ws.zero_row;
   c.num_slots = a.num_slots;
   c.status = ws.status;

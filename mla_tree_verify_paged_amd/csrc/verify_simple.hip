@@ -93,7 +93,7 @@ simple_partial_kernel(RunArgs a, Workspace ws) {
       int ok = 0;
       const int j = j0 + threadIdx.x;
       if (threadIdx.x < n) {
-        const int64_t slot = a.kv_indices[seg.kv0 + j];
+        const int64_t slot = segment_slot(a, seg, j);
         const bool in_range = slot >= 0 && slot < a.num_slots;
         if (!in_range) atomicOr(ws.status, 1u);  // VA_DEV_SLOT_RANGE
         const bool vis = j < seg.P || mrow[j] != 0;
@@ -107,7 +107,7 @@ simple_partial_kernel(RunArgs a, Workspace ws) {
       const int kk = e / kDim, d = e % kDim;
       float v[8];
       if (kk < n && key_ok[kk]) {
-        const int64_t slot = a.kv_indices[seg.kv0 + j0 + kk];
+        const int64_t slot = segment_slot(a, seg, j0 + kk);
         if (kFp32In) {
           const float4 *src =
               reinterpret_cast<const float4 *>(static_cast<const float *>(a.kv) + slot * kDim + d);

@@ -24,7 +24,9 @@ def pool_on_device(w, device="cuda"):
 
 
 def to_device(w, device="cuda", pool=True):
-    """Returns a dict of device tensors for `w` (a workloads.Workload)."""
+    """Returns a dict of device tensors for `w` (a workloads.Workload): the buffers of both
+    slot layouts (tree slots at the tail of each kv_indices segment, and the prefix-only
+    kv_indices with the tree slots in out_cache_loc)."""
     if w.in_dtype == "bf16":
         q = torch.from_numpy(w.q.view(np.int16)).to(device).view(torch.bfloat16)
     else:
@@ -38,6 +40,11 @@ def to_device(w, device="cuda", pool=True):
         custom_mask=torch.from_numpy(mask).to(device),
         mask_indptr=torch.from_numpy(w.mask_indptr).to(device),
     )
+    kvi_p, kvp_p, ocl = w.split_buffers()
+    d["kv_indices_prefix"] = torch.from_numpy(kvi_p if kvi_p.size else np.zeros(1, np.int64)).to(
+        device)
+    d["kv_indptr_prefix"] = torch.from_numpy(kvp_p).to(device)
+    d["out_cache_loc"] = torch.from_numpy(ocl if ocl.size else np.zeros(1, np.int64)).to(device)
     if pool:
         d["kv_buffer"] = pool_on_device(w, device)
     return d

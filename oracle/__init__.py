@@ -41,8 +41,8 @@ def load(path: str = LIB_PATH):
     f = lib.oracle_verify_attn_f64
     f.restype = ctypes.c_int
     vp = ctypes.c_void_p
-    f.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp, vp, ctypes.c_int64,
-                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    f.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int64, vp, vp, vp, vp, vp, vp,
+                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                   ctypes.c_double, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32]
     if path == LIB_PATH:
         _lib = lib
@@ -59,8 +59,11 @@ def _ptr(a):
 
 def verify_attn(q, kv_buffer, kv_indices, kv_indptr, qo_indptr, custom_mask, mask_indptr,
                 num_heads, scale, latent_dim=512, rope_dim=64, rows=None, nthreads=0,
-                lib=None):
+                lib=None, out_cache_loc=None):
     """Runs the oracle. ``q`` and ``kv_buffer`` are bf16 bits (uint16) or float32.
+
+    With ``out_cache_loc`` (int64 [num_tokens]) the kv_indices segments hold the prefix slots
+    only and the tree tokens' slots are taken from ``out_cache_loc``.
 
     Returns (out [n, Dl] float64, lse [n] float64, argmax [n] int64) where n runs over
     ``rows`` (flat t*H + h ids) or over every (token, head) row.
@@ -84,10 +87,14 @@ def verify_attn(q, kv_buffer, kv_indices, kv_indptr, qo_indptr, custom_mask, mas
     qo_indptr = np.ascontiguousarray(qo_indptr, dtype=np.int64)
     custom_mask = np.ascontiguousarray(custom_mask, dtype=np.uint8)
     mask_indptr = np.ascontiguousarray(mask_indptr, dtype=np.int64)
+    if out_cache_loc is not None:
+        out_cache_loc = np.ascontiguousarray(out_cache_loc, dtype=np.int64)
     bs = len(kv_indptr) - 1
     num_tokens = int(qo_indptr[-1]) if bs > 0 else 0
     if q.size != num_tokens * num_heads * d:
         raise ValueError("q does not match qo_indptr")
+    if out_cache_loc is not None and out_cache_loc.size < num_tokens:
+        raise ValueError("out_cache_loc shorter than the token count")
     if rows is not None:
         rows = np.ascontiguousarray(rows, dtype=np.int64)
         n = len(rows)
@@ -99,7 +106,7 @@ def verify_attn(q, kv_buffer, kv_indices, kv_indptr, qo_indptr, custom_mask, mas
     mask_arg = custom_mask if custom_mask.size else np.zeros(1, np.uint8)
     rc = lib.oracle_verify_attn_f64(
         _ptr(q), _ptr(kv_buffer), in_dtype, kv_buffer.size // d, _ptr(kv_indices),
-        _ptr(kv_indptr), _ptr(qo_indptr), _ptr(mask_arg), _ptr(mask_indptr),
+        _ptr(kv_indptr), _ptr(qo_indptr), _ptr(out_cache_loc), _ptr(mask_arg), _ptr(mask_indptr),
         custom_mask.size, bs, num_heads, latent_dim, rope_dim, float(scale), _ptr(rows), n,
         _ptr(out), _ptr(lse), _ptr(am), int(nthreads))
     if rc != 0:
@@ -107,10 +114,16 @@ def verify_attn(q, kv_buffer, kv_indices, kv_indptr, qo_indptr, custom_mask, mas
     return out, lse, am
 
 
-def run_workload(w, rows=None, nthreads=0, pool=None, lib=None):
-    """The oracle on a ``workloads.Workload``."""
+def run_workload(w, rows=None, nthreads=0, pool=None, lib=None, split=False):
+    """The oracle on a ``workloads.Workload`` (with ``split``, given in the prefix /
+    out_cache_loc layout)."""
     if pool is None:
         pool = w.pool_np()
+    if split:
+        kvi, kvp, ocl = w.split_buffers()
+        return verify_attn(w.q, pool, kvi, kvp, w.qo_indptr, w.custom_mask, w.mask_indptr,
+                           w.num_heads, w.scale, rows=rows, nthreads=nthreads, lib=lib,
+                           out_cache_loc=ocl)
     return verify_attn(w.q, pool, w.kv_indices, w.kv_indptr, w.qo_indptr, w.custom_mask,
                        w.mask_indptr, w.num_heads, w.scale, rows=rows, nthreads=nthreads,
                        lib=lib)

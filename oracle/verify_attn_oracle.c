@@ -28,6 +28,14 @@
  *    scalars Dl and Dr are passed separately in "The Final Solder Joint", section "Why the
  *    C-ABI Edit Matters").
  *
+ * Two ways to give the key slots (both from "The Final Solder Joint", section "The
+ * Three-Edits Sequence": prefix slots from kv_indices, the new tokens' slots from
+ * out_cache_loc, told apart by the kv_indptr offsets):
+ *  - out_cache_loc == NULL: request r's L_r keys are kv_indices[kv_indptr[r] .. kv_indptr[r+1]),
+ *    the last T_r of them being the tree tokens in query order;
+ *  - out_cache_loc != NULL: kv_indices[kv_indptr[r] .. kv_indptr[r+1]) holds the P_r prefix
+ *    slots only, and tree key P_r + k is out_cache_loc[qo_indptr[r] + k]; L_r = P_r + T_r.
+ *
  * Readings where the pages are silent (also listed in the design notes):
  *  - tree keys are the last T_r key positions of each request, in query order;
  *  - the mask of request r is a [T_r, L_r] row-major byte matrix at mask_indptr[r]; prefix
@@ -66,17 +74,34 @@ static double elem(const void *base, int dtype, int64_t idx) {
   return (double)((const float *)base)[idx];
 }
 
+/* Number of keys L_r of request r (see the two slot layouts above). */
+static int64_t req_keys(const int32_t *kv_indptr, const int64_t *qo_indptr,
+                        const int64_t *out_cache_loc, int32_t r) {
+  const int64_t n = (int64_t)kv_indptr[r + 1] - (int64_t)kv_indptr[r];
+  return out_cache_loc ? n + (qo_indptr[r + 1] - qo_indptr[r]) : n;
+}
+
+/* Slot of key position j of request r, whose prefix has P keys. */
+static int64_t slot_of(const int64_t *kv_indices, const int32_t *kv_indptr,
+                       const int64_t *qo_indptr, const int64_t *out_cache_loc, int32_t r,
+                       int64_t P, int64_t j) {
+  if (out_cache_loc && j >= P) return out_cache_loc[qo_indptr[r] + (j - P)];
+  return kv_indices[kv_indptr[r] + j];
+}
+
 /* Checks the segment tables: non-decreasing offsets, P_r >= 0, slots in range. */
 static int check_tables(int64_t num_slots, const int64_t *kv_indices,
                         const int32_t *kv_indptr, const int64_t *qo_indptr,
-                        const int64_t *mask_indptr, int64_t mask_len, int32_t bs) {
+                        const int64_t *out_cache_loc, const int64_t *mask_indptr,
+                        int64_t mask_len, int32_t bs) {
   for (int32_t r = 0; r < bs; ++r) {
     int64_t T = qo_indptr[r + 1] - qo_indptr[r];
-    int64_t L = (int64_t)kv_indptr[r + 1] - (int64_t)kv_indptr[r];
-    if (T < 0 || L < 0 || L - T < 0) return ORACLE_ERR_INVALID;
+    int64_t n = (int64_t)kv_indptr[r + 1] - (int64_t)kv_indptr[r];
+    int64_t L = req_keys(kv_indptr, qo_indptr, out_cache_loc, r);
+    if (T < 0 || n < 0 || L - T < 0) return ORACLE_ERR_INVALID;
     if (mask_indptr[r] < 0 || mask_indptr[r] + T * L > mask_len) return ORACLE_ERR_INVALID;
     for (int64_t j = 0; j < L; ++j) {
-      int64_t s = kv_indices[kv_indptr[r] + j];
+      int64_t s = slot_of(kv_indices, kv_indptr, qo_indptr, out_cache_loc, r, L - T, j);
       if (s < 0 || s >= num_slots) return ORACLE_ERR_INVALID;
     }
   }
@@ -85,26 +110,28 @@ static int check_tables(int64_t num_slots, const int64_t *kv_indices,
 
 /*
  * Computes the rows listed in `rows` (flat ids t*H + h), or all num_tokens*H rows when
- * rows == NULL. Outputs are indexed by position in that list: out [n_rows, Dl],
+ * rows == NULL. out_cache_loc may be NULL (see the two slot layouts above). Outputs are indexed by position in that list: out [n_rows, Dl],
  * lse [n_rows], argmax [n_rows]. Returns ORACLE_OK, ORACLE_ERR_INVALID or ORACLE_ERR_NOMEM.
  */
 int oracle_verify_attn_f64(const void *q, const void *kv_buffer, int32_t in_dtype,
                            int64_t num_slots, const int64_t *kv_indices,
                            const int32_t *kv_indptr, const int64_t *qo_indptr,
-                           const uint8_t *custom_mask, const int64_t *mask_indptr,
-                           int64_t mask_len, int32_t bs, int32_t H, int32_t Dl, int32_t Dr,
+                           const int64_t *out_cache_loc, const uint8_t *custom_mask,
+                           const int64_t *mask_indptr, int64_t mask_len, int32_t bs,
+                           int32_t H, int32_t Dl, int32_t Dr,
                            double scale, const int64_t *rows, int64_t n_rows,
                            double *out, double *lse, int64_t *argmax, int32_t nthreads) {
   if (in_dtype != ORACLE_BF16 && in_dtype != ORACLE_FP32) return ORACLE_ERR_INVALID;
   if (bs < 0 || H < 1 || Dl < 1 || Dr < 0) return ORACLE_ERR_INVALID;
-  int rc = check_tables(num_slots, kv_indices, kv_indptr, qo_indptr, mask_indptr, mask_len, bs);
+  int rc = check_tables(num_slots, kv_indices, kv_indptr, qo_indptr, out_cache_loc, mask_indptr,
+                        mask_len, bs);
   if (rc != ORACLE_OK) return rc;
   const int64_t D = (int64_t)Dl + Dr;
   const int64_t num_tokens = bs > 0 ? qo_indptr[bs] : 0;
   const int64_t total = rows ? n_rows : num_tokens * H;
   int64_t max_l = 0;
   for (int32_t r = 0; r < bs; ++r) {
-    int64_t L = (int64_t)kv_indptr[r + 1] - kv_indptr[r];
+    int64_t L = req_keys(kv_indptr, qo_indptr, out_cache_loc, r);
     if (L > max_l) max_l = L;
   }
   for (int64_t n = 0; n < total; ++n) {
@@ -139,7 +166,7 @@ int oracle_verify_attn_f64(const void *q, const void *kv_buffer, int32_t in_dtyp
         while (r + 1 < bs && qo_indptr[r + 1] <= t) ++r;
         const int64_t i = t - qo_indptr[r];
         const int64_t T = qo_indptr[r + 1] - qo_indptr[r];
-        const int64_t L = (int64_t)kv_indptr[r + 1] - kv_indptr[r];
+        const int64_t L = req_keys(kv_indptr, qo_indptr, out_cache_loc, r);
         const int64_t P = L - T;
         const uint8_t *mrow = custom_mask + mask_indptr[r] + i * L;
         const int64_t qbase = (t * H + h) * D;
@@ -150,7 +177,8 @@ int oracle_verify_attn_f64(const void *q, const void *kv_buffer, int32_t in_dtyp
         for (int64_t j = 0; j < L; ++j) {
           vis[j] = (unsigned char)(j < P || mrow[j] != 0);
           if (!vis[j]) continue;
-          const int64_t kbase = kv_indices[kv_indptr[r] + j] * D;
+          const int64_t kbase =
+              slot_of(kv_indices, kv_indptr, qo_indptr, out_cache_loc, r, P, j) * D;
           double dot = 0.0;
           for (int64_t d = 0; d < D; ++d)
             dot += elem(q, in_dtype, qbase + d) * elem(kv_buffer, in_dtype, kbase + d);
@@ -175,7 +203,8 @@ int oracle_verify_attn_f64(const void *q, const void *kv_buffer, int32_t in_dtyp
           if (!vis[j]) continue;
           const double w = exp(s[j] - m);
           lam += w;
-          const int64_t kbase = kv_indices[kv_indptr[r] + j] * D;
+          const int64_t kbase =
+              slot_of(kv_indices, kv_indptr, qo_indptr, out_cache_loc, r, P, j) * D;
           for (int32_t c = 0; c < Dl; ++c) acc[c] += w * elem(kv_buffer, in_dtype, kbase + c);
         }
         for (int32_t c = 0; c < Dl; ++c) o[c] = acc[c] / lam;

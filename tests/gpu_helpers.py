@@ -24,8 +24,10 @@ def say(*a):
 
 
 def run_gpu(w, kernel="auto", num_splits=0, out_dtype="fp32", want_lse=True, want_argmax=True,
-            max_batch=None, max_q_per_req=None, max_q_tokens=None, dev=None, va=None):
-    """Runs workload `w` through the C ABI. Returns (out f64 [rows,512], lse, argmax, status)."""
+            max_batch=None, max_q_per_req=None, max_q_tokens=None, dev=None, va=None,
+            split=False):
+    """Runs workload `w` through the C ABI. Returns (out f64 [rows,512], lse, argmax, status).
+    With `split`, the key slots go in the prefix-only kv_indices plus out_cache_loc layout."""
     import torch
     from mla_tree_verify_paged_amd import VerifyAttn
     from mla_tree_verify_paged_amd.device_inputs import to_device
@@ -44,9 +46,14 @@ def run_gpu(w, kernel="auto", num_splits=0, out_dtype="fp32", want_lse=True, wan
         if want_lse else None
     am = torch.full((n, w.num_heads), -7, dtype=torch.int32, device="cuda") \
         if want_argmax else None
-    va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"], dev["qo_indptr"],
-           dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, am, bs=w.bs,
-           num_tokens=n)
+    if split:
+        va.run(dev["q"], dev["kv_buffer"], dev["kv_indices_prefix"], dev["kv_indptr_prefix"],
+               dev["qo_indptr"], dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, am,
+               bs=w.bs, num_tokens=n, out_cache_loc=dev["out_cache_loc"])
+    else:
+        va.run(dev["q"], dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"], dev["qo_indptr"],
+               dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, am, bs=w.bs,
+               num_tokens=n)
     torch.cuda.synchronize()
     status = va.read_device_status()
     o = out.float().cpu().numpy().astype(np.float64).reshape(n * w.num_heads, 512)
@@ -63,9 +70,9 @@ def sample_rows(w, n, seed=0, must=()):
     return rows.astype(np.int64)
 
 
-def run_oracle(w, rows=None, pool=None):
+def run_oracle(w, rows=None, pool=None, split=False):
     t0 = time.time()
-    res = oracle.run_workload(w, rows=rows, pool=pool)
+    res = oracle.run_workload(w, rows=rows, pool=pool, split=split)
     say(f"  oracle {w.name}: {0 if rows is None else len(rows)} rows in {time.time() - t0:.1f}s")
     return res
 

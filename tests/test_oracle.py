@@ -371,3 +371,33 @@ def test_out_of_range_slot_is_rejected():
     w.kv_indices[3] = w.num_slots
     with pytest.raises(oracle.OracleError):
         run(w, pool)
+
+
+# ------------------------------------------------------- the prefix / out_cache_loc layout
+@pytest.mark.parametrize("seed", range(4))
+def test_split_layout_brute_force(seed):
+    """Prefix slots from kv_indices and tree slots from out_cache_loc name the same keys as
+    the combined layout: the oracle run on the split buffers matches the dense reference
+    built from the combined segments."""
+    rng = np.random.default_rng(2000 + seed)
+    bs = int(rng.integers(2, 5))
+    h = int(rng.choice([1, 3]))
+    t = rng.integers(1, 7, bs)
+    p = rng.integers(0, 120, bs)
+    w = wl.build_workload("split", rng, h, p, t, int((p + t).sum()) + 40)
+    pool = w.pool_np()
+    out, lse, am = oracle.run_workload(w, pool=pool, split=True)
+    ro, rl, ra = dense_reference(w, pool)
+    assert np.max(np.abs(out - ro)) <= 1e-12
+    assert np.max(np.abs(lse - rl) / np.maximum(1.0, np.abs(rl))) <= 1e-12
+    assert np.array_equal(am, ra)
+
+
+def test_split_layout_checks_tree_slots():
+    w = small(7)
+    kvi, kvp, ocl = w.split_buffers()
+    ocl = ocl.copy()
+    ocl[-1] = w.num_slots  # one past the pool
+    with pytest.raises(oracle.OracleError):
+        oracle.verify_attn(w.q, w.pool_np(), kvi, kvp, w.qo_indptr, w.custom_mask,
+                           w.mask_indptr, w.num_heads, w.scale, out_cache_loc=ocl)

@@ -28,8 +28,12 @@ MUTANTS = [
      "custom_mask + mask_indptr[r] + i * T"),
     ("exponent sign flipped", "exp(s[j] - m)", "exp(m - s[j])"),
     ("denominator dropped", "o[c] = acc[c] / lam;", "o[c] = acc[c];"),
-    ("key rows of request 0 for every request", "kv_indices[kv_indptr[r] + j] * D;",
-     "kv_indices[j] * D;"),
+    ("key rows of request 0 for every request", "return kv_indices[kv_indptr[r] + j];",
+     "return kv_indices[j];"),
+    ("tree slots of request 0 for every request", "out_cache_loc[qo_indptr[r] + (j - P)]",
+     "out_cache_loc[j - P]"),
+    ("tree keys left out of the split layout's key count",
+     "return out_cache_loc ? n + (qo_indptr[r + 1] - qo_indptr[r]) : n;", "return n;"),
     ("query row of head 0 for every head", "const int64_t qbase = (t * H + h) * D;",
      "const int64_t qbase = (t * H) * D;"),
 ]
@@ -50,6 +54,7 @@ PINS = [
     pins.test_empty_visible_set,
     pins.test_rope_shift_invariance,
     pins.test_latent_is_the_value_and_rope_only_scores,
+    lambda: pins.test_split_layout_brute_force(0),
 ]
 
 

@@ -149,6 +149,20 @@ class Workload:
         pool[self.kv_indices] = self.kv_rows
         return pool
 
+    def split_buffers(self):
+        """The same key slots in the prefix / out_cache_loc layout: (kv_indices holding each
+        request's prefix slots only, its int32 indptr, out_cache_loc [num_tokens] holding the
+        tree tokens' slots in token order)."""
+        kvi, kvp, ocl = [], [0], []
+        for r in range(self.bs):
+            a, b = int(self.kv_indptr[r]), int(self.kv_indptr[r + 1])
+            p = int(self.prefix_lens[r])
+            kvi.append(self.kv_indices[a:a + p])
+            ocl.append(self.kv_indices[a + p:b])
+            kvp.append(kvp[-1] + p)
+        cat = lambda xs: (np.concatenate(xs) if xs else np.zeros(0)).astype(np.int64)
+        return cat(kvi), np.asarray(kvp, dtype=np.int32), cat(ocl)
+
     def q_f32(self) -> np.ndarray:
         return bf16_bits_to_f32(self.q) if self.in_dtype == "bf16" else self.q
 
