@@ -126,6 +126,48 @@ def cpu_baseline(w, budget_s=15.0):
                       f"all rows"}
 
 
+def time_tree_ops(w, va, steps):
+    """Times the two tree kernels on the workload's trees: the mask build (with mask_indptr)
+    and greedy acceptance (synthetic draft / target tokens that accept about half the time).
+    The mask build is priced against HBM: its algorithmic bytes are the mask it writes plus
+    the parents and index tables it reads."""
+    import torch
+    parents = torch.from_numpy(np.concatenate(w.parents).astype(np.int64)).cuda()
+    qo = torch.from_numpy(w.qo_indptr).cuda()
+    kv = torch.from_numpy(w.kv_indptr).cuda()
+    mask = torch.empty(int(w.mask_indptr[-1]), dtype=torch.uint8, device="cuda")
+    ind = torch.empty(w.bs + 1, dtype=torch.int64, device="cuda")
+    rng = np.random.default_rng(1)
+    draft = rng.integers(0, 4, w.num_tokens).astype(np.int64)
+    target = rng.integers(0, 4, w.num_tokens).astype(np.int64)
+    d_draft, d_target = torch.from_numpy(draft).cuda(), torch.from_numpy(target).cuda()
+    acc = torch.empty(w.bs, dtype=torch.int32, device="cuda")
+    path = torch.empty((w.bs, max(1, w.max_q_per_req)), dtype=torch.int64, device="cuda")
+    nxt = torch.empty(w.bs, dtype=torch.int64, device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    mask_us = timed(lambda: va.build_mask(parents, qo, kv, mask, ind))
+    accept_us = timed(lambda: va.accept(parents, d_draft, d_target, qo, acc, path, nxt))
+    ok = bool(torch.equal(mask.cpu(), torch.from_numpy(w.custom_mask)))
+    mask_bytes = int(w.mask_indptr[-1]) + 8 * w.num_tokens + 20 * (w.bs + 1)
+    return {"mask_build_us": round(mask_us, 3), "mask_bytes": mask_bytes,
+            "mask_build_GBps": round(mask_bytes / (mask_us * 1e-6) / 1e9, 2),
+            "mask_build_frac_hbm": round(mask_bytes / (mask_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "mask_matches_workload": ok, "accept_us": round(accept_us, 3),
+            "timing": "back-to-back launches on torch's current stream, averaged"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +297,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    tree_ops = time_tree_ops(w, va, args.steps)
+    log(f"tree ops: {tree_ops}")
+
     by, fl = algorithmic_work(w)
     traffic = (counter_traffic("mfma_partial_kernel", w.name, ["verify_mfma.hip", "va_internal.h"])
                if kernel_name == "mfma" else None)
@@ -303,6 +348,7 @@ def main():
             "traffic": traffic,
             "kernel": f"{kernel_name} partial (split-K)",
         },
+        "tree_ops": tree_ops,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -92,7 +92,9 @@ enum {
   VA_DEV_SEGMENT = 2u,     /* L_r < T_r, offsets outside kv_indices / mask / q, or a request
                               whose mask segment T_r*L_r reaches 2^31 bytes: rows empty */
   VA_DEV_Q_PER_REQ = 4u,   /* T_r > max_q_per_req: the request's rows written empty         */
-  VA_DEV_TOKENS = 8u       /* qo_indptr[bs] != num_tokens: uncovered rows written empty     */
+  VA_DEV_TOKENS = 8u,      /* qo_indptr[bs] != num_tokens: uncovered rows written empty     */
+  VA_DEV_TREE = 16u        /* a tree parent index that does not precede its child (-1: root)
+                              (verify_attn_build_mask, verify_attn_accept)                  */
 };
 
 typedef struct {
@@ -165,6 +167,59 @@ va_status verify_attn_set_profiling_events(verify_attn_ctx *ctx, void *before, v
 
 /* Reports the fixed launch configuration of a context. */
 va_status verify_attn_get_info(const verify_attn_ctx *ctx, verify_attn_info *info);
+
+/*
+ * Builds the verify mask from the draft trees on `stream` (capture-safe: kernels only). The
+ * mask is rebuilt from the tree structure ("The Glue That Binds", section "The Thinking
+ * Process"), in the layout verify_attn_run reads.
+ *   parents      int64 [num_tokens]: for tree token t of request r (node i = t - qo_indptr[r]),
+ *                the node index of its parent within the request, -1 for a root. A parent must
+ *                precede its child; one that does not sets VA_DEV_TREE and ends that node's
+ *                ancestor chain there.
+ *   qo_indptr    int64 [bs+1]; kv_indptr int32 [bs+1]: as for verify_attn_run, with
+ *                split_layout != 0 meaning kv_indptr counts prefix keys only (tree slots in
+ *                out_cache_loc), so that L_r = P_r + T_r.
+ *   custom_mask  uint8 [mask_len]: request r's [T_r, L_r] row-major matrix at mask_indptr[r];
+ *                row i gets 1 in every prefix column j < P_r and, in column P_r + k, 1 iff
+ *                node k is node i or one of its ancestors. Rows whose segment does not fit
+ *                mask_len (or whose request is malformed) are left unwritten and set
+ *                VA_DEV_SEGMENT.
+ *   mask_indptr  int64 [bs+1]: read, or first written as the running sum of T_r * L_r from 0
+ *                when write_mask_indptr != 0.
+ * Host-checked: ctx, 0 <= bs <= max_batch, 0 <= num_tokens <= max_q_tokens, the context's
+ * max_q_per_req <= 2048 (else VA_ERR_UNSUPPORTED), pointers when bs > 0.
+ */
+va_status verify_attn_build_mask(verify_attn_ctx *ctx, const int64_t *parents,
+                                 const int64_t *qo_indptr, const int32_t *kv_indptr,
+                                 int32_t split_layout, int32_t bs, int64_t num_tokens,
+                                 uint8_t *custom_mask, int64_t mask_len, int64_t *mask_indptr,
+                                 int32_t write_mask_indptr, void *stream);
+
+/*
+ * Greedy acceptance of the verified trees on `stream` (capture-safe). The library exposes tree
+ * acceptance next to verify attention ("The Glue That Connects", section "What the Edit
+ * Actually Does"); no algorithm is given there, so this is the plain greedy rule: node 0 of each
+ * request is the root (the last accepted token); from it, the walk moves to the lowest-indexed
+ * child whose draft token equals the target's token at the current node, until none matches.
+ *   parents        int64 [num_tokens], as for verify_attn_build_mask.
+ *   draft_tokens   int64 [num_tokens]: the token each tree node proposes.
+ *   target_tokens  int64 [num_tokens]: the target model's token at each tree node (its argmax
+ *                  after the model head).
+ *   accept_len     int32 [bs]: accepted draft nodes (the path without the root).
+ *   accept_path    int64 [bs, max_path]: the path's node indices, root first, -1 after it
+ *                  (truncated to max_path).
+ *   next_token     int64 [bs]: the target's token at the last node of the path.
+ * A request without tree tokens gets 0, an all -1 path and -1; a malformed request sets
+ * VA_DEV_SEGMENT and gets the same. A parent that does not precede its child sets VA_DEV_TREE;
+ * that request's output is then unspecified (but every write stays in its rows).
+ * Host-checked: ctx, 0 <= bs <= max_batch, 0 <= num_tokens <= max_q_tokens, max_path >= 1,
+ * max_q_per_req <= 2048, pointers when bs > 0.
+ */
+va_status verify_attn_accept(verify_attn_ctx *ctx, const int64_t *parents,
+                             const int64_t *draft_tokens, const int64_t *target_tokens,
+                             const int64_t *qo_indptr, int32_t bs, int64_t num_tokens,
+                             int32_t *accept_len, int64_t *accept_path, int32_t max_path,
+                             int64_t *next_token, void *stream);
 
 /* Frees the context and any workspace it allocated. NULL is a no-op. */
 void verify_attn_destroy(verify_attn_ctx *ctx);

@@ -19,12 +19,13 @@ LIB_PATH = os.environ.get("VERIFY_ATTN_LIB", os.path.join(_HERE, "libverify_attn
 VA_OK, VA_ERR_NULL, VA_ERR_INVALID, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = range(6)
 VA_BF16, VA_FP32 = 0, 1
 VA_KERNEL_AUTO, VA_KERNEL_SIMPLE, VA_KERNEL_MFMA = 0, 1, 2
-VA_DEV_SLOT_RANGE, VA_DEV_SEGMENT, VA_DEV_Q_PER_REQ, VA_DEV_TOKENS = 1, 2, 4, 8
+VA_DEV_SLOT_RANGE, VA_DEV_SEGMENT, VA_DEV_Q_PER_REQ, VA_DEV_TOKENS, VA_DEV_TREE = 1, 2, 4, 8, 16
 
 EXPORTED = (
     "verify_attn_workspace_bytes", "verify_attn_create", "verify_attn_run",
     "verify_attn_read_device_status", "verify_attn_set_profiling_events",
     "verify_attn_get_info", "verify_attn_destroy", "verify_attn_last_error",
+    "verify_attn_build_mask", "verify_attn_accept",
 )
 
 
@@ -73,6 +74,10 @@ def _load(path: str = LIB_PATH):
     lib.verify_attn_set_profiling_events.restype = ctypes.c_int
     lib.verify_attn_get_info.argtypes = [vp, ctypes.POINTER(verify_attn_info)]
     lib.verify_attn_get_info.restype = ctypes.c_int
+    lib.verify_attn_build_mask.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, i64, vp, i32, vp]
+    lib.verify_attn_build_mask.restype = ctypes.c_int
+    lib.verify_attn_accept.argtypes = [vp, vp, vp, vp, vp, i32, i64, vp, vp, i32, vp, vp]
+    lib.verify_attn_accept.restype = ctypes.c_int
     lib.verify_attn_destroy.argtypes = [vp]
     lib.verify_attn_destroy.restype = None
     lib.verify_attn_last_error.argtypes = []
@@ -120,6 +125,23 @@ def verify_attn_run(ctx, q, kv_buffer, num_slots, kv_indices, num_kv_indices, kv
                                kv_indptr, qo_indptr, custom_mask, mask_len, mask_indptr,
                                out_cache_loc, bs, num_tokens, sm_scale, out, out_lse,
                                out_argmax, stream))
+
+
+def verify_attn_build_mask(ctx, parents, qo_indptr, kv_indptr, split_layout, bs, num_tokens,
+                           custom_mask, mask_len, mask_indptr, write_mask_indptr,
+                           stream) -> None:
+    """Pointer-level call: every buffer argument is a device address (int) or None."""
+    _check(lib.verify_attn_build_mask(ctx, parents, qo_indptr, kv_indptr, split_layout, bs,
+                                      num_tokens, custom_mask, mask_len, mask_indptr,
+                                      write_mask_indptr, stream))
+
+
+def verify_attn_accept(ctx, parents, draft_tokens, target_tokens, qo_indptr, bs, num_tokens,
+                       accept_len, accept_path, max_path, next_token, stream) -> None:
+    """Pointer-level call: every buffer argument is a device address (int) or None."""
+    _check(lib.verify_attn_accept(ctx, parents, draft_tokens, target_tokens, qo_indptr, bs,
+                                  num_tokens, accept_len, accept_path, max_path, next_token,
+                                  stream))
 
 
 def verify_attn_read_device_status(ctx, stream=None) -> int:
@@ -189,6 +211,40 @@ class VerifyAttn:
                         int(num_tokens),
                         float(sm_scale), _ptr(out), _ptr(out_lse), _ptr(out_argmax), stream)
         return out
+
+    def build_mask(self, parents, qo_indptr, kv_indptr, custom_mask, mask_indptr,
+                   split_layout=False, write_mask_indptr=True, bs=None, num_tokens=None,
+                   stream=None):
+        """Builds the verify mask from the tree parents into `custom_mask` (and, by default,
+        writes `mask_indptr`)."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        if bs is None:
+            bs = qo_indptr.numel() - 1
+        if num_tokens is None:
+            num_tokens = parents.numel()
+        verify_attn_build_mask(self.ctx, _ptr(parents), _ptr(qo_indptr), _ptr(kv_indptr),
+                               int(bool(split_layout)), int(bs), int(num_tokens),
+                               _ptr(custom_mask), custom_mask.numel(), _ptr(mask_indptr),
+                               int(bool(write_mask_indptr)), stream)
+        return custom_mask
+
+    def accept(self, parents, draft_tokens, target_tokens, qo_indptr, accept_len, accept_path,
+               next_token, bs=None, num_tokens=None, stream=None):
+        """Greedy acceptance: fills accept_len [bs], accept_path [bs, max_path] and
+        next_token [bs]."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        if bs is None:
+            bs = qo_indptr.numel() - 1
+        if num_tokens is None:
+            num_tokens = parents.numel()
+        verify_attn_accept(self.ctx, _ptr(parents), _ptr(draft_tokens), _ptr(target_tokens),
+                           _ptr(qo_indptr), int(bs), int(num_tokens), _ptr(accept_len),
+                           _ptr(accept_path), int(accept_path.shape[1]), _ptr(next_token),
+                           stream)
 
     def read_device_status(self, stream=None) -> int:
         import torch

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libverify_attn.so")
-SOURCES = ["capi.cpp", "verify_simple.hip", "verify_mfma.hip", "verify_combine.hip"]
+SOURCES = ["capi.cpp", "verify_simple.hip", "verify_mfma.hip", "verify_combine.hip",
+           "tree_ops.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -252,6 +252,77 @@ va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_bu
   return ok();
 }
 
+va_status verify_attn_build_mask(verify_attn_ctx *ctx, const int64_t *parents,
+                                 const int64_t *qo_indptr, const int32_t *kv_indptr,
+                                 int32_t split_layout, int32_t bs, int64_t num_tokens,
+                                 uint8_t *custom_mask, int64_t mask_len, int64_t *mask_indptr,
+                                 int32_t write_mask_indptr, void *stream) {
+  if (!ctx) return fail(VA_ERR_NULL, "ctx is NULL");
+  if (bs < 0 || bs > ctx->cfg.max_batch)
+    return fail(VA_ERR_INVALID, "bs %d out of range [0, %d]", bs, ctx->cfg.max_batch);
+  if (num_tokens < 0 || num_tokens > ctx->cfg.max_q_tokens)
+    return fail(VA_ERR_INVALID, "num_tokens %lld out of range [0, %lld]",
+                (long long)num_tokens, (long long)ctx->cfg.max_q_tokens);
+  if (ctx->cfg.max_q_per_req > va::kMaxTreeNodes)
+    return fail(VA_ERR_UNSUPPORTED, "max_q_per_req above %d", va::kMaxTreeNodes);
+  if (mask_len < 0) return fail(VA_ERR_INVALID, "mask_len must be >= 0");
+  if (bs == 0) return ok();
+  if (!qo_indptr || !kv_indptr || !mask_indptr || (num_tokens > 0 && (!parents || !custom_mask)))
+    return fail(VA_ERR_NULL, "a required pointer is NULL");
+  va::TreeArgs a;
+  a.parents = parents;
+  a.qo_indptr = qo_indptr;
+  a.kv_indptr = kv_indptr;
+  a.split_layout = split_layout != 0;
+  a.bs = bs;
+  a.num_tokens = num_tokens;
+  a.max_q_per_req = ctx->cfg.max_q_per_req;
+  a.mask = custom_mask;
+  a.mask_len = mask_len;
+  a.mask_indptr = mask_indptr;
+  a.status = ctx->ws.status;
+  const hipError_t e =
+      va::launch_build_mask(a, write_mask_indptr != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VA_ERR_HIP, "mask build launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+va_status verify_attn_accept(verify_attn_ctx *ctx, const int64_t *parents,
+                             const int64_t *draft_tokens, const int64_t *target_tokens,
+                             const int64_t *qo_indptr, int32_t bs, int64_t num_tokens,
+                             int32_t *accept_len, int64_t *accept_path, int32_t max_path,
+                             int64_t *next_token, void *stream) {
+  if (!ctx) return fail(VA_ERR_NULL, "ctx is NULL");
+  if (bs < 0 || bs > ctx->cfg.max_batch)
+    return fail(VA_ERR_INVALID, "bs %d out of range [0, %d]", bs, ctx->cfg.max_batch);
+  if (num_tokens < 0 || num_tokens > ctx->cfg.max_q_tokens)
+    return fail(VA_ERR_INVALID, "num_tokens %lld out of range [0, %lld]",
+                (long long)num_tokens, (long long)ctx->cfg.max_q_tokens);
+  if (max_path < 1) return fail(VA_ERR_INVALID, "max_path must be >= 1");
+  if (ctx->cfg.max_q_per_req > va::kMaxTreeNodes)
+    return fail(VA_ERR_UNSUPPORTED, "max_q_per_req above %d", va::kMaxTreeNodes);
+  if (bs == 0) return ok();
+  if (!qo_indptr || !accept_len || !accept_path || !next_token ||
+      (num_tokens > 0 && (!parents || !draft_tokens || !target_tokens)))
+    return fail(VA_ERR_NULL, "a required pointer is NULL");
+  va::AcceptArgs a;
+  a.parents = parents;
+  a.draft_tokens = draft_tokens;
+  a.target_tokens = target_tokens;
+  a.qo_indptr = qo_indptr;
+  a.bs = bs;
+  a.num_tokens = num_tokens;
+  a.max_q_per_req = ctx->cfg.max_q_per_req;
+  a.accept_len = accept_len;
+  a.accept_path = accept_path;
+  a.max_path = max_path;
+  a.next_token = next_token;
+  a.status = ctx->ws.status;
+  const hipError_t e = va::launch_accept(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VA_ERR_HIP, "accept launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 va_status verify_attn_read_device_status(verify_attn_ctx *ctx, void *stream, uint32_t *flags) {
   if (!ctx || !flags) return fail(VA_ERR_NULL, "ctx or flags is NULL");
   hipStream_t st = static_cast<hipStream_t>(stream);

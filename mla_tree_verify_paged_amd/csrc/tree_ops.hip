@@ -1,0 +1,204 @@
+// tree_ops.hip - the steps around verify attention that work on the draft trees themselves:
+// building the verify mask from the parent array, and greedy acceptance.
+//
+// The library that exposes verify attention also exposes tree building and tree acceptance
+// ("The Glue That Connects: Wiring a Custom Flash Attention Kernel into the C-ABI Layer",
+// section "What the Edit Actually Does"); the mask is rebuilt from the tree structure rather
+// than decoded from a packed format ("The Glue That Binds: Wiring a Custom CUDA Kernel into
+// Production via C-ABI", section "The Thinking Process"). The acceptance rule is the plain
+// greedy one (no algorithm is given): from the root, follow the lowest-indexed child whose
+// draft token equals the target's token at the current node.
+//
+// Both are small integer kernels: every output is exact.
+#include "va_internal.h"
+
+namespace va {
+namespace {
+
+constexpr int kMaskThreads = 256;
+constexpr int kScanThreads = 256;
+
+// (T, L, P) of request r for either slot layout; false if the segment is not usable.
+__device__ __forceinline__ bool tree_shape(const TreeArgs &a, int r, int64_t &q0, int32_t &T,
+                                           int32_t &L, int32_t &P) {
+  q0 = a.qo_indptr[r];
+  const int64_t q1 = a.qo_indptr[r + 1];
+  const int64_t n = int64_t(a.kv_indptr[r + 1]) - int64_t(a.kv_indptr[r]);
+  const int64_t t = q1 - q0;
+  const int64_t l = a.split_layout ? n + t : n;
+  if (t < 0 || n < 0 || q0 < 0 || q1 > a.num_tokens || l < t || l > INT32_MAX ||
+      t > a.max_q_per_req)
+    return false;
+  T = int32_t(t);
+  L = int32_t(l);
+  P = int32_t(l - t);
+  return true;
+}
+
+// mask_indptr[r+1] = sum over requests <= r of T_r * L_r (0 for an unusable request).
+__global__ void __launch_bounds__(kScanThreads) mask_indptr_kernel(TreeArgs a) {
+  __shared__ int64_t part[kScanThreads];
+  int64_t carry = 0;
+  if (threadIdx.x == 0) a.mask_indptr[0] = 0;
+  for (int base = 0; base < a.bs; base += kScanThreads) {
+    const int r = base + int(threadIdx.x);
+    int64_t v = 0;
+    if (r < a.bs) {
+      int64_t q0;
+      int32_t T, L, P;
+      if (tree_shape(a, r, q0, T, L, P)) v = int64_t(T) * L;
+    }
+    part[threadIdx.x] = v;
+    __syncthreads();
+    // inclusive scan (Hillis-Steele)
+    for (int o = 1; o < kScanThreads; o <<= 1) {
+      const int64_t x = threadIdx.x >= unsigned(o) ? part[threadIdx.x - o] : 0;
+      __syncthreads();
+      part[threadIdx.x] += x;
+      __syncthreads();
+    }
+    if (r < a.bs) a.mask_indptr[r + 1] = carry + part[threadIdx.x];
+    carry += part[kScanThreads - 1];
+    __syncthreads();
+  }
+}
+
+// One workgroup per mask row (tree token t).
+__global__ void __launch_bounds__(kMaskThreads) build_mask_kernel(TreeArgs a) {
+  extern __shared__ int32_t tree_smem[];  // parents [max_q_per_req], then ancestor flags
+  int32_t *par = tree_smem;
+  int32_t *anc = tree_smem + a.max_q_per_req;
+  const int64_t t = blockIdx.x;
+  if (t >= a.num_tokens) return;
+  // the request that owns token t: the last r with qo_indptr[r] <= t
+  int lo = 0, hi = a.bs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.qo_indptr[mid] <= t) lo = mid; else hi = mid;
+  }
+  int64_t q0;
+  int32_t T, L, P;
+  bool ok = a.bs > 0 && tree_shape(a, lo, q0, T, L, P) && t >= q0 && t < q0 + T;
+  const int64_t m0 = ok ? a.mask_indptr[lo] : 0;
+  if (ok && (m0 < 0 || m0 + int64_t(T) * L > a.mask_len)) ok = false;
+  if (!ok) {
+    if (threadIdx.x == 0) atomicOr(a.status, 2u);  // VA_DEV_SEGMENT: row not written
+    return;
+  }
+  const int i = int(t - q0);
+  for (int k = threadIdx.x; k < T; k += kMaskThreads) {
+    const int64_t p = a.parents[q0 + k];
+    par[k] = (p >= -1 && p < k) ? int32_t(p) : -2;  // -2: does not precede its child
+    anc[k] = 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int node = i;
+    bool bad = false;
+    for (int steps = 0; steps <= T && node >= 0; ++steps) {
+      anc[node] = 1;
+      const int p = par[node];
+      if (p == -2) { bad = true; break; }
+      node = p;
+    }
+    if (bad) atomicOr(a.status, 16u);  // VA_DEV_TREE
+  }
+  __syncthreads();
+
+  uint8_t *row = a.mask + m0 + int64_t(i) * L;
+  // prefix columns: ones, 16 bytes per store once the address is aligned
+  const int head = min(int((16 - (reinterpret_cast<uintptr_t>(row) & 15)) & 15), P);
+  for (int x = threadIdx.x; x < head; x += kMaskThreads) row[x] = 1;
+  const int body = (P - head) / 16;
+  uint4 *row16 = reinterpret_cast<uint4 *>(row + head);
+  for (int x = threadIdx.x; x < body; x += kMaskThreads)
+    row16[x] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+  for (int x = head + 16 * body + int(threadIdx.x); x < P; x += kMaskThreads) row[x] = 1;
+  // tree columns: node k is visible iff it is node i or one of its ancestors
+  for (int k = threadIdx.x; k < T; k += kMaskThreads) row[P + k] = uint8_t(anc[k]);
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// One wavefront per request.
+__global__ void __launch_bounds__(64) accept_kernel(AcceptArgs a) {
+  extern __shared__ int64_t acc_smem[];  // parents, draft and target tokens [max_q_per_req]
+  int64_t *par = acc_smem;
+  int64_t *drf = acc_smem + a.max_q_per_req;
+  int64_t *tgt = acc_smem + 2 * a.max_q_per_req;
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t q0 = a.qo_indptr[r], q1 = a.qo_indptr[r + 1];
+  const int64_t tt = q1 - q0;
+  int64_t *path = a.accept_path + int64_t(r) * a.max_path;
+  const bool ok = tt >= 0 && q0 >= 0 && q1 <= a.num_tokens && tt <= a.max_q_per_req;
+  if (!ok || tt == 0) {
+    if (!ok && lane == 0) atomicOr(a.status, 2u);  // VA_DEV_SEGMENT
+    for (int k = lane; k < a.max_path; k += 64) path[k] = -1;
+    if (lane == 0) {
+      a.accept_len[r] = 0;
+      a.next_token[r] = -1;
+    }
+    return;
+  }
+  const int T = int(tt);
+  bool bad = false;
+  for (int k = lane; k < T; k += 64) {
+    const int64_t p = a.parents[q0 + k];
+    bad |= p < -1 || p >= k;  // a parent must precede its child
+    par[k] = p;
+    drf[k] = a.draft_tokens[q0 + k];
+    tgt[k] = a.target_tokens[q0 + k];
+  }
+  if (__ballot(bad) != 0 && lane == 0) atomicOr(a.status, 16u);  // VA_DEV_TREE
+  __syncthreads();
+  // With parents preceding children every step moves to a higher node, so the walk ends
+  // within T steps; the bound also ends it on a malformed tree (whose output is unspecified).
+  int cur = 0, len = 0;
+  if (lane == 0 && a.max_path > 0) path[0] = 0;
+  for (int steps = 0; steps < T; ++steps) {
+    const int64_t want = tgt[cur];
+    int best = 0x7fffffff;
+    for (int c = lane; c < T; c += 64)
+      if (par[c] == cur && drf[c] == want) best = min(best, c);
+    best = wave_min(best);
+    if (best == 0x7fffffff) break;
+    cur = best;
+    ++len;
+    if (lane == 0 && len < a.max_path) path[len] = cur;
+  }
+  for (int k = len + 1 + lane; k < a.max_path; k += 64) path[k] = -1;
+  if (lane == 0) {
+    a.accept_len[r] = len;
+    a.next_token[r] = tgt[cur];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_build_mask(const TreeArgs &a, bool write_indptr, hipStream_t st) {
+  if (write_indptr) {
+    hipLaunchKernelGGL(mask_indptr_kernel, dim3(1), dim3(kScanThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.num_tokens <= 0) return hipSuccess;
+  if (a.num_tokens > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const size_t smem = size_t(2) * a.max_q_per_req * sizeof(int32_t);
+  hipLaunchKernelGGL(build_mask_kernel, dim3(unsigned(a.num_tokens)), dim3(kMaskThreads), smem,
+                     st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const AcceptArgs &a, hipStream_t st) {
+  if (a.bs <= 0) return hipSuccess;
+  const size_t smem = size_t(3) * a.max_q_per_req * sizeof(int64_t);
+  hipLaunchKernelGGL(accept_kernel, dim3(unsigned(a.bs)), dim3(64), smem, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace va

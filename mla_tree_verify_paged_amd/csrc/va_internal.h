@@ -114,6 +114,40 @@ __device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segmen
   return 0u;
 }
 
+// Arguments of the mask build (see include/verify_attn.h).
+struct TreeArgs {
+  const int64_t *parents;
+  const int64_t *qo_indptr;
+  const int32_t *kv_indptr;
+  int32_t split_layout;  // kv_indptr counts prefix keys only (tree slots in out_cache_loc)
+  int32_t bs;
+  int64_t num_tokens;
+  int32_t max_q_per_req;
+  uint8_t *mask;
+  int64_t mask_len;
+  int64_t *mask_indptr;
+  uint32_t *status;
+};
+
+// Arguments of the greedy acceptance.
+struct AcceptArgs {
+  const int64_t *parents;
+  const int64_t *draft_tokens;
+  const int64_t *target_tokens;
+  const int64_t *qo_indptr;
+  int32_t bs;
+  int64_t num_tokens;
+  int32_t max_q_per_req;
+  int32_t *accept_len;
+  int64_t *accept_path;
+  int32_t max_path;
+  int64_t *next_token;
+  uint32_t *status;
+};
+
+// Largest tree the tree kernels stage in LDS.
+constexpr int kMaxTreeNodes = 2048;
+
 // Slot of key position j (0 <= j < L) of a validated segment.
 __device__ __forceinline__ int64_t segment_slot(const RunArgs &a, const Segment &s, int j) {
   return (s.tree && j >= s.P) ? s.tree[j - s.P] : a.kv_indices[s.kv0 + j];
@@ -125,6 +159,8 @@ hipError_t launch_simple_partial(const RunArgs &a, const Workspace &ws, int in_f
 hipError_t launch_mfma_partial(const RunArgs &a, const Workspace &ws, int rows_per_block,
                                hipStream_t st);
 hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st);
+hipError_t launch_build_mask(const TreeArgs &a, bool write_indptr, hipStream_t st);
+hipError_t launch_accept(const AcceptArgs &a, hipStream_t st);
 
 // Rows per workgroup of each partial kernel (fixes the grid).
 constexpr int kSimpleHeadsPerBlock = 4;
