@@ -149,10 +149,14 @@ __device__ __forceinline__ void matrix_drain() {
 // lds + 16*l. Inline assembly so that the compiler does not track the LDS write (it would
 // otherwise wait for these loads before every LDS read); the kernel waits for them itself
 // before the data is read, and a barrier orders them for the other wavefronts.
+// The scalar base comes from v_readlane just before: a vector-memory instruction that reads
+// an SGPR written by a VALU instruction needs 5 wait states on this generation, and the
+// compiler does not look inside the asm, so the asm supplies them (s_mov + s_nop 4 = 6; they
+// also cover the M0 write before the LDS DMA).
 __device__ __forceinline__ void dma_row(uint64_t base, uint32_t voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
       : "v"(voff), "s"(base), "s"(lds)
