@@ -168,13 +168,17 @@ def time_tree_ops(w, va, steps):
             "timing": "back-to-back launches on torch's current stream, averaged"}
 
 
+def workload_names():
+    import workloads
+    return workloads.CONFIGS.keys()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="long",
-                    choices=["tiny", "short", "long", "segmented", "stress"])
+    ap.add_argument("--workload", default="long", choices=sorted(workload_names()))
     ap.add_argument("--kernel", default="auto", choices=["auto", "simple", "mfma"])
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--layout", default="combined", choices=["combined", "split"],
@@ -305,7 +309,15 @@ def main():
                if kernel_name == "mfma" else None)
     part_s = part_ms.mean() * 1e-3
     us = ms_per_step * 1e3
-    achieved = fl / part_s / 1e12
+    # the binding roofline of the step: matrix work, or the bytes when few query rows share
+    # each key row; the partial kernel moves everything but the output, which the combine
+    # writes
+    hbm_bound = by / (PEAK_HBM_GBS * 1e9) > fl / (PEAK_MFMA_TFLOPS * 1e12)
+    part_bytes = by - w.num_tokens * w.num_heads * 512 * 4
+    if hbm_bound:
+        achieved, peak, unit = part_bytes / part_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = fl / part_s / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s"
     result = {
         "metric": METRIC,
         "value": round(us, 3),
@@ -340,11 +352,11 @@ def main():
                           "p10": round(float(np.percentile(cold, 10)), 3),
                           "p90": round(float(np.percentile(cold, 90)), 3)},
         "roofline": {
-            "bound": "mfma",
+            "bound": "hbm" if hbm_bound else "mfma",
             "achieved": round(achieved, 3),
-            "peak": PEAK_MFMA_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel": f"{kernel_name} partial (split-K)",
         },

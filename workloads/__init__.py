@@ -22,7 +22,7 @@ position P_r + k is query token k itself. Prefix columns of the mask are filled 
 tree columns hold ancestor-or-self visibility.
 
 Draw order for every workload (numpy ``default_rng(seed)``):
-  1. segmented batch only: prefix lengths, then tree sizes;
+  1. batched workloads only: prefix lengths, then tree sizes;
   2. per request, the tree parents;
   3. the pool slots (distinct);
   4. q ~ N(0,1) float32 [num_tokens, H, 576];
@@ -285,7 +285,25 @@ def stress(seed: int = 0) -> Workload:
                           max_depth=8, spike_frac=0.01)
 
 
-CONFIGS = {"tiny": tiny, "short": short, "long": long, "segmented": segmented, "stress": stress}
+# ----------------------------------------------------------------------------- few rows per request
+# One GPU's share of the heads under 8-way tensor parallelism (H = 64 / 8) with small draft trees:
+# few query rows per request, so the key rows' bytes decide the time rather than the matrix work.
+def tp8(seed: int = 0) -> Workload:
+    """1 request, H=8, P=23,000, T=4 random tree, bf16, rope dims x0.5, 1,048,576-slot pool."""
+    rng = np.random.default_rng(seed)
+    return build_workload("tp8", rng, 8, [23_000], [4], 1_048_576, rope_scale=0.5)
+
+
+def tp8_batch(seed: int = 0) -> Workload:
+    """32 requests, H=8, P_r log-uniform in [1024, 32768], T_r uniform in {1, 2, 3, 4}, bf16."""
+    rng = np.random.default_rng(seed)
+    p = np.floor(np.exp(rng.uniform(math.log(1024), math.log(32768), 32))).astype(np.int64)
+    t = rng.integers(1, 5, 32).astype(np.int64)
+    return build_workload("tp8_batch", rng, 8, p, t, 1_048_576)
+
+
+CONFIGS = {"tiny": tiny, "short": short, "long": long, "segmented": segmented, "stress": stress,
+           "tp8": tp8, "tp8_batch": tp8_batch}
 
 
 def make(name: str, seed: int = 0) -> Workload:
