@@ -26,6 +26,8 @@ struct verify_attn_ctx {
   int32_t splits;
   int32_t rows_per_block;
   int32_t row_tiles_per_req;
+  int32_t grid;       // MFMA partial kernel: workgroups (one per compute unit)
+  int64_t part_rows;  // partial rows the workspace holds
   size_t ws_bytes;
   void *ws_base;
   bool ws_owned;
@@ -54,9 +56,27 @@ va_status ok() {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Compute units of the current device (the MFMA partial kernel runs one workgroup on each);
+// 256, MI355X's count, when no device answers.
+int32_t compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
+
+struct Derived {
+  int32_t kernel, splits, rows_per_block, row_tiles, grid;
+  int64_t part_rows;
+  size_t bytes;
+};
+
 // Checks a config and fills the derived launch parameters. Returns VA_OK or an error.
-va_status derive(const verify_attn_config *c, int32_t *kernel, int32_t *splits,
-                 int32_t *rows_per_block, int32_t *row_tiles, size_t *bytes) {
+va_status derive(const verify_attn_config *c, Derived *d) {
   if (!c) return fail(VA_ERR_NULL, "config is NULL");
   if (c->num_heads < 1 || c->num_heads > 4096)
     return fail(VA_ERR_INVALID, "num_heads %d out of range [1, 4096]", c->num_heads);
@@ -81,40 +101,46 @@ va_status derive(const verify_attn_config *c, int32_t *kernel, int32_t *splits,
   if (k == VA_KERNEL_MFMA && c->in_dtype != VA_BF16)
     return fail(VA_ERR_UNSUPPORTED, "the MFMA kernel takes bf16 inputs only");
 
-  int32_t rpb, tiles;
-  int64_t blocks_per_split;
-  if (k == VA_KERNEL_SIMPLE) {
-    rpb = va::kSimpleHeadsPerBlock;
-    tiles = int32_t(int64_t(c->max_q_per_req) * ceil_div(c->num_heads, rpb));
-  } else {
-    rpb = va::kMfmaRowsPerBlock;
-    tiles = int32_t(ceil_div(int64_t(c->max_q_per_req) * c->num_heads, rpb));
-  }
-  blocks_per_split = int64_t(c->max_batch) * tiles;
-  int32_t s = c->num_splits;
-  if (s == 0) {
-    // enough workgroups to cover the 256 compute units once (MFMA) or several times
-    const int64_t target = k == VA_KERNEL_MFMA ? 256 : 2048;
-    s = int32_t(ceil_div(target, blocks_per_split));
-    if (s < 1) s = 1;
-    if (s > 64) s = 64;
-  }
-  if (blocks_per_split * s > 0x7fffffffLL)
-    return fail(VA_ERR_INVALID, "launch grid too large");
   const int64_t rows_cap = c->max_q_tokens * c->num_heads;
-  size_t off[5];
-  *bytes = va::workspace_layout(s, rows_cap, off);
-  *kernel = k;
-  *splits = s;
-  *rows_per_block = rpb;
-  *row_tiles = tiles;
+  int32_t s = c->num_splits;
+  d->grid = 0;
+  if (k == VA_KERNEL_SIMPLE) {
+    d->rows_per_block = va::kSimpleHeadsPerBlock;
+    d->row_tiles =
+        int32_t(int64_t(c->max_q_per_req) * ceil_div(c->num_heads, va::kSimpleHeadsPerBlock));
+    const int64_t blocks_per_split = int64_t(c->max_batch) * d->row_tiles;
+    if (s == 0) {
+      // enough workgroups to cover the compute units several times
+      s = int32_t(ceil_div(2048, blocks_per_split));
+      if (s < 1) s = 1;
+      if (s > 64) s = 64;
+    }
+    if (blocks_per_split * s > 0x7fffffffLL)
+      return fail(VA_ERR_INVALID, "launch grid too large");
+    d->part_rows = int64_t(s) * rows_cap;
+  } else {
+    d->rows_per_block = va::kMfmaRowsPerBlock;
+    d->row_tiles = int32_t(ceil_div(int64_t(c->max_q_per_req) * c->num_heads,
+                                    va::kMfmaRowsPerBlock));
+    // With s == 0 the work list is balanced on the device so that it holds at most `grid`
+    // items (one per compute unit, a multiple of 8) of kMfmaRowsPerBlock rows each when the
+    // requests have fewer row tiles than that (else one item per row tile), which bounds the
+    // partial rows by kMfmaRowsPerBlock * grid + rows_cap.
+    d->grid = int32_t(ceil_div(compute_units(), 8) * 8);
+    d->part_rows = s == 0 ? int64_t(va::kMfmaRowsPerBlock) * d->grid + rows_cap
+                          : int64_t(s) * rows_cap;
+  }
+  size_t off[6];
+  d->bytes = va::workspace_layout(d->part_rows, rows_cap, off);
+  d->kernel = k;
+  d->splits = s;
   return VA_OK;
 }
 
 void bind_workspace(verify_attn_ctx *x) {
-  size_t off[5];
+  size_t off[6];
   const int64_t rows_cap = x->cfg.max_q_tokens * x->cfg.num_heads;
-  va::workspace_layout(x->splits, rows_cap, off);
+  va::workspace_layout(x->part_rows, rows_cap, off);
   char *b = static_cast<char *>(x->ws_base);
   x->ws.status = reinterpret_cast<uint32_t *>(b + off[0]);
   x->ws.zero_row = reinterpret_cast<const uint16_t *>(b + off[0] + va::kZeroRowOffset);
@@ -122,6 +148,8 @@ void bind_workspace(verify_attn_ctx *x) {
   x->ws.part_lse = reinterpret_cast<float *>(b + off[2]);
   x->ws.part_max = reinterpret_cast<float *>(b + off[3]);
   x->ws.part_arg = reinterpret_cast<int32_t *>(b + off[4]);
+  x->ws.row_info = reinterpret_cast<va::RowInfo *>(b + off[5]);
+  x->ws.part_rows = x->part_rows;
   x->ws.rows_cap = rows_cap;
   x->ws.splits = x->splits;
 }
@@ -131,19 +159,18 @@ void bind_workspace(verify_attn_ctx *x) {
 extern "C" {
 
 size_t verify_attn_workspace_bytes(const verify_attn_config *cfg) {
-  int32_t k, s, rpb, tiles;
-  size_t bytes = 0;
-  if (derive(cfg, &k, &s, &rpb, &tiles, &bytes) != VA_OK) return 0;
-  return bytes;
+  Derived d;
+  if (derive(cfg, &d) != VA_OK) return 0;
+  return d.bytes;
 }
 
 va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **out) {
   if (!out) return fail(VA_ERR_NULL, "out is NULL");
   *out = nullptr;
-  int32_t k, s, rpb, tiles;
-  size_t bytes = 0;
-  va_status st = derive(cfg, &k, &s, &rpb, &tiles, &bytes);
+  Derived d;
+  va_status st = derive(cfg, &d);
   if (st != VA_OK) return st;
+  const size_t bytes = d.bytes;
   void *base = cfg->workspace;
   bool owned = false;
   if (base) {
@@ -169,10 +196,12 @@ va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **ou
     return fail(VA_ERR_INVALID, "out of host memory");
   }
   x->cfg = *cfg;
-  x->kernel = k;
-  x->splits = s;
-  x->rows_per_block = rpb;
-  x->row_tiles_per_req = tiles;
+  x->kernel = d.kernel;
+  x->splits = d.splits;
+  x->rows_per_block = d.rows_per_block;
+  x->row_tiles_per_req = d.row_tiles;
+  x->grid = d.grid;
+  x->part_rows = d.part_rows;
   x->ws_bytes = bytes;
   x->ws_base = base;
   x->ws_owned = owned;
@@ -238,7 +267,7 @@ va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_bu
     if (ctx->kernel == VA_KERNEL_SIMPLE)
       e = va::launch_simple_partial(a, ctx->ws, ctx->cfg.in_dtype == VA_FP32, st);
     else
-      e = va::launch_mfma_partial(a, ctx->ws, ctx->rows_per_block, st);
+      e = va::launch_mfma_partial(a, ctx->ws, ctx->rows_per_block, ctx->grid, st);
     if (e != hipSuccess)
       return fail(VA_ERR_HIP, "partial kernel launch failed: %s", hipGetErrorString(e));
   }

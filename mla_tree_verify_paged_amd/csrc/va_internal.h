@@ -1,14 +1,17 @@
 // va_internal.h - declarations shared by the library's translation units (not installed).
 //
-// Workspace layout (all offsets 256-byte aligned), for S splits and R = max_q_tokens * H rows:
+// Workspace layout (all offsets 256-byte aligned), for a capacity of N partial rows and
+// R = max_q_tokens * H output rows:
 //   status   uint32 [64]            sticky VA_DEV_* bits in word 0
 //   zero_row uint16 [576]           zeros; key rows that must not be read load from here
-//   part_o   float  [S][R][512]     per-split normalised output O_s
-//   part_lse float  [S][R]          per-split log-sum-exp (natural log); -inf for an empty split
-//   part_max float  [S][R]          per-split max score (natural-log units)
-//   part_arg int32  [S][R]          per-split argmax key position (-1 when empty)
-// A partial row (s, t*H+h) is written by the partial kernel for every split s of the request
-// that owns token t, including empty splits, whenever the request's segment is valid.
+//   part_o   float  [N][512]        per-split normalised output O_s
+//   part_lse float  [N]             per-split log-sum-exp (natural log); -inf for an empty split
+//   part_max float  [N]             per-split max score (natural-log units)
+//   part_arg int32  [N]             per-split argmax key position (-1 when empty)
+//   row_info RowInfo [R]            where output row x's partials are (see RowInfo)
+// Request r's partials are one block of n_r * R_r rows (R_r = T_r * H): split k of its local
+// row x is partial row base_r + k * R_r + x. The partial kernel writes, for every valid
+// request, all n_r splits of every row and the row_info of every row.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,6 +25,13 @@ constexpr int kRope = 64;
 constexpr int kDim = kLatent + kRope;  // 576
 constexpr int kMaxSplits = 256;
 
+// Where the partials of one output row are: split k (k < n) is partial row base + k * stride.
+struct RowInfo {
+  int64_t base;
+  int32_t n;
+  int32_t stride;
+};
+
 struct Workspace {
   uint32_t *status;
   const uint16_t *zero_row;
@@ -29,8 +39,10 @@ struct Workspace {
   float *part_lse;
   float *part_max;
   int32_t *part_arg;
-  int64_t rows_cap;  // R
-  int32_t splits;    // S
+  RowInfo *row_info;
+  int64_t part_rows;  // N, the partial rows the workspace holds
+  int64_t rows_cap;   // R
+  int32_t splits;     // key splits per request; 0: chosen per call on the device (MFMA)
 };
 
 // Arguments of one verify step, as the kernels see them.
@@ -66,13 +78,16 @@ constexpr size_t kZeroRowOffset = kStatusBytes;
 constexpr size_t kHeaderBytes = kZeroRowOffset + kDim * sizeof(uint16_t);
 
 // Byte offsets of the workspace regions for S splits and R rows; returns the total size.
-inline size_t workspace_layout(int32_t S, int64_t R, size_t off[5]) {
+// Byte offsets of the workspace regions for N partial rows and R output rows; returns the
+// total size.
+inline size_t workspace_layout(int64_t N, int64_t R, size_t off[6]) {
   size_t o = 0;
   off[0] = o; o = align256(o + kHeaderBytes);
-  off[1] = o; o = align256(o + size_t(S) * size_t(R) * kLatent * sizeof(float));
-  off[2] = o; o = align256(o + size_t(S) * size_t(R) * sizeof(float));
-  off[3] = o; o = align256(o + size_t(S) * size_t(R) * sizeof(float));
-  off[4] = o; o = align256(o + size_t(S) * size_t(R) * sizeof(int32_t));
+  off[1] = o; o = align256(o + size_t(N) * kLatent * sizeof(float));
+  off[2] = o; o = align256(o + size_t(N) * sizeof(float));
+  off[3] = o; o = align256(o + size_t(N) * sizeof(float));
+  off[4] = o; o = align256(o + size_t(N) * sizeof(int32_t));
+  off[5] = o; o = align256(o + size_t(R) * sizeof(RowInfo));
   return o;
 }
 
@@ -157,7 +172,7 @@ __device__ __forceinline__ int64_t segment_slot(const RunArgs &a, const Segment 
 hipError_t launch_simple_partial(const RunArgs &a, const Workspace &ws, int in_fp32,
                                  hipStream_t st);
 hipError_t launch_mfma_partial(const RunArgs &a, const Workspace &ws, int rows_per_block,
-                               hipStream_t st);
+                               int grid, hipStream_t st);
 hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st);
 hipError_t launch_build_mask(const TreeArgs &a, bool write_indptr, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t st);

@@ -8,12 +8,14 @@
 // and the argmax is the argmax of the split holding the largest max score (lowest split,
 // hence lowest key position, on ties).
 //
-// Two wavefronts per row, each lane owning 4 output dims: the per-split scalars are read
-// lane-parallel (lane s holds split s), then the 16-byte slices of up to 32 splits with
-// nonzero weight are loaded at once, so the partial rows of every split are in flight
-// together. The combine also owns output validation: a row whose token belongs to no valid
-// request is written empty (out 0, lse -inf, argmax -1) and the matching status bit is set,
-// so every output element is defined whatever the device-side tables hold.
+// One workgroup per row. Every wavefront reads the per-split scalars lane-parallel (lane s
+// holds split s) and derives the same max, weights and argmax; the splits' partial rows are
+// dealt to the four wavefronts (split s to wavefront s % 4), each lane owning 8 output dims,
+// with up to 8 splits' rows in flight per wavefront; the four partial sums meet in LDS. A row
+// with many splits (few rows, long keys) is thus read by 256 threads. The combine also owns
+// output validation: a row whose token belongs to no valid request is written empty (out 0,
+// lse -inf, argmax -1) and the matching status bit is set, so every output element is defined
+// whatever the device-side tables hold.
 #include <math.h>
 
 #include "va_internal.h"
@@ -22,9 +24,8 @@ namespace va {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kThreadsPerRow = 128;                     // 4 dims each
-constexpr int kRowsPerBlock = kThreads / kThreadsPerRow;
-constexpr int kBatch = 32;                              // splits whose slices are in flight
+constexpr int kWaves = kThreads / 64;
+constexpr int kBatch = 8;  // splits whose rows a wavefront has in flight
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -55,66 +56,93 @@ __device__ void store4(const RunArgs &a, int64_t row, int dim0, const float4 &v)
   }
 }
 
+__device__ __forceinline__ void fma8(float4 &lo, float4 &hi, float w, const float4 &x0,
+                                     const float4 &x1) {
+  lo.x = fmaf(w, x0.x, lo.x); lo.y = fmaf(w, x0.y, lo.y);
+  lo.z = fmaf(w, x0.z, lo.z); lo.w = fmaf(w, x0.w, lo.w);
+  hi.x = fmaf(w, x1.x, hi.x); hi.y = fmaf(w, x1.y, hi.y);
+  hi.z = fmaf(w, x1.z, hi.z); hi.w = fmaf(w, x1.w, hi.w);
+}
+
 __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace ws) {
+  __shared__ float4 red[kWaves - 1][kLatent / 4];
   const int lane = threadIdx.x & 63;
-  const int sub = threadIdx.x % kThreadsPerRow;            // 0..127 within the row
-  const bool lead = sub == 0;                              // writes the row's scalars
-  const int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
-  if (row >= a.num_tokens * a.H) return;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
   const int64_t t = row / a.H;
-  const int dim0 = 4 * sub;
-  const int S = ws.splits;
-  const int64_t stride = ws.rows_cap;
-  const float *plse = ws.part_lse + row;
-  const float *pmax = ws.part_max + row;
+
+  // where this row's partials are (written by the partial kernel for every row of a valid
+  // request; for other rows it is stale or arbitrary, so it is only used once checked to stay
+  // inside the workspace, and such rows are discarded below)
+  const RowInfo ri = ws.row_info[row];
+  int S = ri.n;
+  int64_t base = ri.base, stride = ri.stride;
+  const bool placed = S >= 1 && S <= (1 << 20) && stride >= 1 && stride <= (1 << 28) &&
+                      base >= 0 && base + int64_t(S - 1) * stride < ws.part_rows;
+  if (!placed) {
+    S = 0;
+    base = 0;
+    stride = 0;
+  }
+  const float *plse = ws.part_lse + base;
+  const float *pmax = ws.part_max + base;
+  // lane l holds 8 dims: [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4)
+  const float *po = ws.part_o + base * kLatent + 4 * lane;
+  const int64_t ostride = stride * kLatent;
 
   // Requested before the row is validated, so that one memory round trip serves all of them:
-  // the slices of the first kBatch splits and the scalars of the first 64. Every address is
-  // inside the workspace (row < num_tokens * H <= rows_cap); an invalid row discards them.
-  float4 x[kBatch];
+  // this wavefront's first kBatch splits and the scalars of the first 64 (all inside the
+  // workspace, as checked above).
+  float4 x0[kBatch], x1[kBatch];
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k)
-    x[k] = k < S ? *reinterpret_cast<const float4 *>(ws.part_o + (int64_t(k) * stride + row) *
-                                                                     kLatent + dim0)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
-  const float lse0 = lane < S ? plse[lane * stride] : -INFINITY;
-  const float max0 = lane < S ? pmax[lane * stride] : -INFINITY;
+  for (int j = 0; j < kBatch; ++j) {
+    const int sp = wave + kWaves * j;
+    if (sp < S) {
+      x0[j] = *reinterpret_cast<const float4 *>(po + sp * ostride);
+      x1[j] = *reinterpret_cast<const float4 *>(po + sp * ostride + 256);
+    }
+  }
+  const float lse0 = lane < S ? plse[int64_t(lane) * stride] : -INFINITY;
+  const float max0 = lane < S ? pmax[int64_t(lane) * stride] : -INFINITY;
 
   // the request that owns token t: the last r with qo_indptr[r] <= t
-  int lo = 0, hi = a.bs;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.qo_indptr[mid] <= t) lo = mid; else hi = mid;
-  }
   uint32_t bad = 0;
-  bool ok = a.bs > 0;
+  bool ok = a.bs > 0 && row < a.num_tokens * a.H;
   if (ok) {
+    int lo = 0, hi = a.bs;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.qo_indptr[mid] <= t) lo = mid; else hi = mid;
+    }
     Segment seg;
     bad = load_segment(a, lo, seg);
     ok = bad == 0 && t >= seg.q0 && t < seg.q0 + seg.T;
     if (bad == 0 && !ok) bad = 8u;  // VA_DEV_TOKENS
+    if (ok && !placed) {  // cannot happen: the partial kernel places every valid row
+      ok = false;
+      bad = 2u;
+    }
   } else {
     bad = 8u;
   }
-
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (!ok) {
-    if (lead) {
+    if (threadIdx.x == 0) {
       atomicOr(ws.status, bad);
       if (a.out_lse) a.out_lse[row] = -INFINITY;
       if (a.out_argmax) a.out_argmax[row] = -1;
     }
-    store4(a, row, dim0, v);
+    if (threadIdx.x < kLatent / 4) store4(a, row, 4 * threadIdx.x, make_float4(0.f, 0.f, 0.f, 0.f));
     return;
   }
 
-  // per-split scalars, lane-parallel (lane s holds split s, then s + 64, ...)
+  // per-split scalars, lane-parallel (lane s holds split s, then s + 64, ...); every
+  // wavefront computes the same M, best and W
   float M = lse0, best = max0;
   for (int s0 = 64; s0 < S; s0 += 64) {
     const int s = s0 + lane;
     if (s < S) {
-      M = fmaxf(M, plse[s * stride]);
-      best = fmaxf(best, pmax[s * stride]);
+      M = fmaxf(M, plse[int64_t(s) * stride]);
+      best = fmaxf(best, pmax[int64_t(s) * stride]);
     }
   }
   M = wave_max(M);
@@ -122,46 +150,61 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
 
   float W = 0.f;
   int arg = -1;
+  float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
   if (M != -INFINITY) {
-    for (int s0 = 0; s0 < S; s0 += kBatch) {
-      // lane j < kBatch: the weight of split s0 + j
+    for (int s0 = 0; s0 < S; s0 += 64) {
       const int s = s0 + lane;
-      // splits below 64 come from lane s of the speculative read, the rest from memory
-      const float lsh = __shfl(lse0, s & 63, 64);
-      float ls = -INFINITY;
-      if (lane < kBatch && s < S) ls = s < 64 ? lsh : plse[s * stride];
+      const float ls = s < 64 ? (s < S ? lse0 : -INFINITY)
+                              : (s < S ? plse[int64_t(s) * stride] : -INFINITY);
       const float wgt = ls == -INFINITY ? 0.f : expf(ls - M);
       W += wave_sum(wgt);
-      if (arg < 0) {  // wave-uniform
-        const uint64_t hit = __ballot(lane < kBatch && s < S && pmax[s * stride] == best);
-        if (hit) arg = ws.part_arg[(s0 + __builtin_ctzll(hit)) * stride + row];
+      if (arg < 0) {  // wave-uniform: the lowest split holding the largest max score
+        const float mx = s < 64 ? max0 : (s < S ? pmax[int64_t(s) * stride] : -INFINITY);
+        const uint64_t hit = __ballot(s < S && mx == best);
+        if (hit) arg = ws.part_arg[base + int64_t(s0 + __builtin_ctzll(hit)) * stride];
       }
-      const uint32_t live = uint32_t(__ballot(wgt != 0.f));
-      if (s0 > 0) {
+      // this wavefront's splits of the 64: s0 + wave + 4j, in batches of kBatch
+      for (int j0 = 0; j0 < 64 / kWaves; j0 += kBatch) {
+        if (s0 + wave + kWaves * j0 >= S) break;
+        if (s0 > 0 || j0 > 0) {
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          if ((live >> k) & 1u)
-            x[k] = *reinterpret_cast<const float4 *>(
-                ws.part_o + (int64_t(s0 + k) * stride + row) * kLatent + dim0);
-          else
-            x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+          for (int j = 0; j < kBatch; ++j) {
+            const int sp = s0 + wave + kWaves * (j0 + j);
+            if (sp < S) {
+              x0[j] = *reinterpret_cast<const float4 *>(po + sp * ostride);
+              x1[j] = *reinterpret_cast<const float4 *>(po + sp * ostride + 256);
+            }
+          }
         }
-      }
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        // a split with zero weight contributes nothing (its slice is not read, or is zero)
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), k));
-        if ((live >> k) & 1u) {
-          v.x = fmaf(wk, x[k].x, v.x); v.y = fmaf(wk, x[k].y, v.y);
-          v.z = fmaf(wk, x[k].z, v.z); v.w = fmaf(wk, x[k].w, v.w);
+        for (int j = 0; j < kBatch; ++j) {
+          const int sl = wave + kWaves * (j0 + j);  // lane of this split within the 64
+          const float wk = __shfl(wgt, sl, 64);
+          // a split with zero weight contributes nothing (its row may be unwritten)
+          if (s0 + sl < S && wk != 0.f) fma8(acc0, acc1, wk, x0[j], x1[j]);
         }
       }
     }
-    const float inv = 1.f / W;
-    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
   }
-  store4(a, row, dim0, v);
-  if (lead) {
+  // the four wavefronts' sums meet in LDS; wavefront 0 finishes the row
+  if (wave > 0) {
+    red[wave - 1][lane] = acc0;
+    red[wave - 1][64 + lane] = acc1;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int k = 0; k < kWaves - 1; ++k) {
+    const float4 r0 = red[k][lane], r1 = red[k][64 + lane];
+    acc0.x += r0.x; acc0.y += r0.y; acc0.z += r0.z; acc0.w += r0.w;
+    acc1.x += r1.x; acc1.y += r1.y; acc1.z += r1.z; acc1.w += r1.w;
+  }
+  const float inv = M == -INFINITY ? 0.f : 1.f / W;
+  acc0.x *= inv; acc0.y *= inv; acc0.z *= inv; acc0.w *= inv;
+  acc1.x *= inv; acc1.y *= inv; acc1.z *= inv; acc1.w *= inv;
+  store4(a, row, 4 * lane, acc0);
+  store4(a, row, 256 + 4 * lane, acc1);
+  if (lane == 0) {
     if (a.out_lse) a.out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
     if (a.out_argmax) a.out_argmax[row] = arg;
   }
@@ -172,9 +215,8 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
 hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st) {
   const int64_t rows = a.num_tokens * a.H;
   if (rows <= 0) return hipSuccess;
-  const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, st, a, ws);
+  if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(rows)), dim3(kThreads), 0, st, a, ws);
   return hipGetLastError();
 }
 

@@ -36,6 +36,7 @@
 //    share its L2; HBM then sees each latent row about once.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "va_internal.h"
@@ -79,10 +80,19 @@ static_assert(kRowsPerWave == 8, "one rope load instruction covers 8 rows");
 static_assert(kRawTile % 16 == 0 && kVOff % 16 == 0, "16-byte aligned tiles");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
+// The narrow path (items of at most 32 rows) adds a 16 KB partial-score exchange buffer:
+// [wave][quad][lane] float4.
+constexpr int kXOff = kLdsBytes;
+constexpr int kXBytes = kWaves * 4 * 64 * 16;
+static_assert(kXOff + kXBytes <= 160 * 1024, "LDS budget of the narrow path");
+
 // LDS: raw bf16 tiles 0 and 1 (latent rows at a padded stride, then the rope block), then
-// fp16 latent tiles 0 and 1; the usable-key bits of the two raw tiles (a byte per wave).
-__shared__ __attribute__((aligned(16))) char g_lds[kLdsBytes];
+// fp16 latent tiles 0 and 1, then the narrow path's exchange buffer; the usable-key bits of
+// the two raw tiles (a byte per wave).
+__shared__ __attribute__((aligned(16))) char g_lds[kXOff + kXBytes];
 __shared__ uint32_t g_okbits[2];
+// the narrow path's key slots of two tiles, loaded straight into LDS: [tile parity][wave][8]
+__shared__ __attribute__((aligned(16))) int64_t g_slots[2][kWaves][kRowsPerWave];
 
 __device__ __forceinline__ uint32_t lds_addr(const char *p) {
   return uint32_t(reinterpret_cast<uintptr_t>(p));
@@ -183,6 +193,21 @@ __device__ __forceinline__ void wait_tile_loads() {
 // and vector-memory loads complete in issue order, so tile 0 and q have landed.
 __device__ __forceinline__ void wait_loads_but_tile1() {
   asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+}
+// The same, leaving 10 loads in flight (the narrow path's slot load plus a tile's 9).
+__device__ __forceinline__ void wait_loads_but_10() {
+  asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+}
+// One global_load_lds_dword per lane from a per-lane address: lane l's 4 bytes land at
+// lds + 4*l.
+__device__ __forceinline__ void dma_dword_lanes(const void *src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(src), "s"(lds)
+      : "memory", "m0");
 }
 
 // Per-workgroup constants of one split.
@@ -378,7 +403,9 @@ __device__ __forceinline__ float neg_max(const RowState &st) {
   return st.m == -INFINITY ? 0.f : -st.m;
 }
 
-template <int K>
+// kCompute = false: a wavefront whose 32 rows all lie past the request's rows only does its
+// share of the tile staging (conversion, loads, slot fetch); the others need that share.
+template <int K, bool kCompute = true>
 __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const StepIO &io,
                                      const TileLoads &tl, int64_t &slot_vec, int slot_tile,
                                      const bf16x8 *qf, f32x16 *o, f32x16 &snext,
@@ -398,7 +425,7 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
   f32x16 sa, sb;  // the two score chains
   const float negm = neg_max(st);
 
-  if constexpr (K == kLast) {
+  if constexpr (K == kLast && kCompute) {
 #pragma unroll
     for (int part = 0; part < 8; ++part) p_part(part, scur, c2, negm, st.lsum, pf);
   }
@@ -406,7 +433,7 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
   // operand fragment of operation p
   auto load = [&](auto pc) __attribute__((always_inline)) {
     constexpr int p = decltype(pc)::value;
-    if constexpr (p < N) {
+    if constexpr (p < N && kCompute) {
       constexpr Op op = T.op[p];
       u32x4 r;
       if constexpr (!op.pv) {
@@ -436,7 +463,8 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
     constexpr Op op = T.op[p];
     load(std::integral_constant<int, p + kDepth>{});
     const u32x4 a = fr[p % (kDepth + 1)];
-    if constexpr (op.pv) {
+    if constexpr (!kCompute) {
+    } else if constexpr (op.pv) {
       constexpr int ch = op.idx / kDBlocks, d = op.idx % kDBlocks;
       pv_mfma(o[d], a, pf[ch]);
     } else {
@@ -455,7 +483,7 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
       }
     }
     // phase A: P(t), two keys after each of the first eight fragments
-    if constexpr (K == kMain && p < 8) p_part(p, scur, c2, negm, st.lsum, pf);
+    if constexpr (K == kMain && kCompute && p < 8) p_part(p, scur, c2, negm, st.lsum, pf);
     // the loads of tile t+2 (zero rows past the split), then the slots of tile t+3
     if constexpr (K == kMain) {
       constexpr int dp = p - Plan::kDmaOp;
@@ -476,7 +504,7 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
       });
     }
     // merge of the two score chains
-    if constexpr (K == kMain) {
+    if constexpr (K == kMain && kCompute) {
       constexpr int mp = p - Plan::kMergeOp;
       if constexpr (mp >= 0) {
 #pragma unroll
@@ -485,14 +513,14 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
     }
     __builtin_amdgcn_sched_barrier(0);
   });
-  if constexpr (K == kFirst) {
+  if constexpr (K == kFirst && kCompute) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) snext[e] = sa[e] + sb[e];
   }
 }
 
 // ---- the rest of the softmax of one tile's scores: mask, max (and argmax), lazy rescale
-template <bool kArgmax>
+template <bool kArgmax, int kOBlocks = kDBlocks>
 __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits, f32x16 &sacc,
                                           f32x16 *o, RowState &st, float c2, bool row_ok,
                                           const uint8_t *mseg, uint32_t moff) {
@@ -500,6 +528,10 @@ __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits,
   // of row `col`. Masking is skipped for tiles of usable prefix keys only.
   const bool tail = kb + kTK > c.P;
   if (tail || okbits != 0xffffffffu) {
+    // key of accumulator e: jh + 8*(e/4) + e%4 (the lane-dependent part folded into jh and
+    // okh, so that the per-e offsets are constants)
+    const int jh = kb + 4 * c.half;
+    const uint32_t okh = okbits >> (4 * c.half);
     uint32_t tree_vis = 0xffffffffu;
     if (tail) {
       // the lane's row's mask bytes (addresses clamped into the row; keys past the split
@@ -507,20 +539,19 @@ __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits,
       uint8_t mb[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int j = kb + 8 * (e >> 2) + 4 * c.half + (e & 3);
+        const int j = jh + 8 * (e >> 2) + (e & 3);
         mb[e] = mseg[moff + uint32_t(min(j, c.k1 - 1))];
       }
       tree_vis = 0;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int j = kb + 8 * (e >> 2) + 4 * c.half + (e & 3);
+        const int j = jh + 8 * (e >> 2) + (e & 3);
         tree_vis |= uint32_t(j < c.P || (row_ok && mb[e] != 0)) << e;
       }
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int kk = 8 * (e >> 2) + 4 * c.half + (e & 3);
-      const bool vis = ((okbits >> kk) & 1u) && ((tree_vis >> e) & 1u);
+      const bool vis = ((okh >> (8 * (e >> 2) + (e & 3))) & 1u) && ((tree_vis >> e) & 1u);
       sacc[e] = vis ? sacc[e] : -INFINITY;
     }
   }
@@ -557,34 +588,230 @@ __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits,
     st.lsum *= alpha;
     matrix_drain();
 #pragma unroll
-    for (int d = 0; d < kDBlocks; ++d) scale_acc(o[d], alpha);
+    for (int d = 0; d < kOBlocks; ++d) scale_acc(o[d], alpha);
     matrix_drain();
   }
 }
 
-template <bool kArgmax>
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
-  // ---- XCD-aware work mapping: consecutive work items land on one XCD
-  const int nb = gridDim.x;  // a multiple of 8
-  const int w = (int(blockIdx.x) & 7) * (nb >> 3) + (int(blockIdx.x) >> 3);
-  if (w >= n_work) return;
-  const int S = ws.splits;
-  const int tile = w % tiles_per_req;
-  const int s = (w / tiles_per_req) % S;
-  const int r = w / (tiles_per_req * S);
-
+// ---- the balanced work list
+//
+// Request r (a usable segment with T_r > 0) has rt_r = ceil(T_r H / 128) row tiles and
+// kt_r = ceil(L_r / 32) key tiles. Its keys are cut into n_r splits of ct_r key tiles (the
+// last one may be shorter), and a work item is one (split, row tile) pair. Items are
+// numbered request by request, split-major with the row tile fastest, so consecutive items
+// (which the launch places on one XCD) read the same key rows. Every workgroup computes the
+// same plan from the index tables, with no host involvement:
+//  * a fixed split count S: ct_r = ceil(kt_r / S);
+//  * otherwise one common ct for every request, the smallest for which the batch has at most
+//    G items (G = the grid, one workgroup per compute unit), so each workgroup gets one item
+//    and the largest item is as small as the cut allows; when the requests have G row tiles
+//    or more, one split per request.
+// The launch has a workgroup for every item. Partial rows: request r's n_r * T_r H rows
+// follow those of the requests before it.
+struct ReqWork {
   Segment seg;
-  const uint32_t bad = load_segment(a, r, seg);
-  if (bad) {
-    if (threadIdx.x == 0 && tile == 0 && s == 0) atomicOr(ws.status, bad);
-    return;
+  int32_t rows;  // T_r * H; 0 when the request has nothing to compute
+  int32_t rt;    // row tiles
+  int32_t kt;    // key tiles
+  uint32_t bad;  // VA_DEV_* bits of an unusable segment
+};
+
+__device__ __forceinline__ ReqWork req_work(const RunArgs &a, int r) {
+  ReqWork q;
+  q.rows = q.rt = q.kt = 0;
+  q.bad = 0;
+  q.seg.T = q.seg.L = q.seg.P = 0;
+  q.seg.q0 = q.seg.kv0 = q.seg.m0 = 0;
+  q.seg.tree = nullptr;
+  if (r < a.bs) {
+    q.bad = load_segment(a, r, q.seg);
+    if (q.bad == 0 && q.seg.T > 0) {
+      q.rows = q.seg.T * a.H;  // T <= 65536, H <= 4096
+      q.rt = (q.rows + kRows - 1) / kRows;
+      q.kt = (q.seg.L - 1) / kTK + 1;  // L >= T >= 1
+    }
   }
+  return q;
+}
+
+// Key tiles per split, and the split count, of a request under the plan (c, forced).
+__device__ __forceinline__ int split_tiles(int kt, int c, int forced) {
+  return forced > 0 ? (kt + forced - 1) / forced : min(c, kt);
+}
+__device__ __forceinline__ int split_count(const ReqWork &q, int c, int forced) {
+  if (q.rt == 0) return 0;
+  const int ct = split_tiles(q.kt, c, forced);
+  return (q.kt + ct - 1) / ct;
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+struct WorkPlan {
+  int c;          // key tiles per split (common cut)
+  int forced;     // splits per request (0: common cut)
+  int64_t items;  // work items in all
+};
+
+// Request base + lane: chunk 0 comes from the lane's cached request when kCached.
+template <bool kCached>
+__device__ __forceinline__ ReqWork chunk_request(const RunArgs &a, const ReqWork &mine,
+                                                 int base, int lane) {
+  if (kCached && base == 0) return mine;
+  return req_work(a, base + lane);
+}
+
+__device__ int64_t count_items(const RunArgs &a, const ReqWork &mine, int c, int forced,
+                               int lane) {
+  int64_t n = 0;
+  for (int base = 0; base < a.bs; base += 64) {
+    const ReqWork q = chunk_request<true>(a, mine, base, lane);
+    n += wave_sum64(int64_t(q.rt) * split_count(q, c, forced));
+  }
+  return uniform(n);
+}
+
+__device__ WorkPlan plan_work(const RunArgs &a, const ReqWork &mine, int G, int forced,
+                              uint32_t *status, bool report, int lane) {
+  WorkPlan p;
+  p.c = 1;
+  p.forced = forced;
+  int64_t C = 0, RT = 0;
+  int ktmax = 0;
+  for (int base = 0; base < a.bs; base += 64) {
+    const ReqWork q = chunk_request<true>(a, mine, base, lane);
+    if (report && q.bad) atomicOr(status, q.bad);
+    C += wave_sum64(int64_t(q.rt) * q.kt);
+    RT += wave_sum64(int64_t(q.rt));
+    ktmax = max(ktmax, wave_max_int(q.kt));
+  }
+  C = uniform(C);
+  RT = uniform(RT);
+  ktmax = uniform(ktmax);
+  if (forced > 0 || C == 0) {
+    p.items = C == 0 ? 0 : count_items(a, mine, 1, forced, lane);
+    return p;
+  }
+  int64_t c = (C + G - 1) / G;
+  if (RT >= G) {
+    c = ktmax;
+  } else if (count_items(a, mine, int(min(c, int64_t(ktmax))), 0, lane) > G) {
+    // items(c) <= C / c + RT, so ceil(C / (G - RT)) tiles per split fit G items; the count
+    // does not grow with c: bisect for the smallest c that fits
+    int64_t lo = c, hi = (C + (G - RT) - 1) / (G - RT);
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (count_items(a, mine, int(min(mid, int64_t(ktmax))), 0, lane) <= G) hi = mid;
+      else lo = mid;
+    }
+    c = hi;
+  }
+  p.c = int(min(c, int64_t(ktmax)));
+  p.items = count_items(a, mine, p.c, 0, lane);
+  return p;
+}
+
+struct Item {
+  Segment seg;
+  int rows;      // T_r * H
+  int rt;        // row tile
+  int k;         // split
+  int n;         // splits of the request
+  int ct;        // key tiles per split
+  int64_t prow;  // the request's first partial row
+};
+
+__device__ __forceinline__ Segment uniform(const Segment &s) {
+  Segment u;
+  u.q0 = uniform(s.q0);
+  u.T = uniform(s.T);
+  u.L = uniform(s.L);
+  u.P = uniform(s.P);
+  u.kv0 = uniform(s.kv0);
+  u.m0 = uniform(s.m0);
+  u.tree = s.tree;
+  return u;
+}
+
+template <bool kCached>
+__device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan &p, int64_t w,
+                          int lane, Item &it) {
+  int64_t first = 0, prow = 0;
+  for (int base = 0; base < a.bs; base += 64) {
+    const ReqWork q = chunk_request<kCached>(a, mine, base, lane);
+    const int n = split_count(q, p.c, p.forced);
+    const int64_t items = int64_t(q.rt) * n;
+    const int64_t prows = int64_t(n) * q.rows;
+    const int64_t si = wave_inclusive_scan64(items, lane);
+    const int64_t sp = wave_inclusive_scan64(prows, lane);
+    const int64_t lo = first + si - items;
+    const uint64_t hit = __ballot(items > 0 && lo <= w && w < lo + items);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      if (lane == l) {
+        const int64_t local = w - lo;
+        it.seg = q.seg;
+        it.rows = q.rows;
+        it.rt = int(local % q.rt);
+        it.k = int(local / q.rt);
+        it.n = n;
+        it.ct = split_tiles(q.kt, p.c, p.forced);
+        it.prow = prow + sp - prows;
+      }
+      // lane l's values to every lane (and to scalar registers)
+      it.seg.q0 = __shfl(it.seg.q0, l, 64);
+      it.seg.T = __shfl(it.seg.T, l, 64);
+      it.seg.L = __shfl(it.seg.L, l, 64);
+      it.seg.P = __shfl(it.seg.P, l, 64);
+      it.seg.kv0 = __shfl(it.seg.kv0, l, 64);
+      it.seg.m0 = __shfl(it.seg.m0, l, 64);
+      it.seg = uniform(it.seg);
+      // rebuilt from the kernel argument rather than moved between lanes, so that the
+      // compiler still knows it points to global memory (it would otherwise use flat loads)
+      it.seg.tree = a.out_cache_loc ? a.out_cache_loc + it.seg.q0 : nullptr;
+      it.rows = uniform(__shfl(it.rows, l, 64));
+      it.rt = uniform(__shfl(it.rt, l, 64));
+      it.k = uniform(__shfl(it.k, l, 64));
+      it.n = uniform(__shfl(it.n, l, 64));
+      it.ct = uniform(__shfl(it.ct, l, 64));
+      it.prow = uniform(__shfl(it.prow, l, 64));
+      return true;
+    }
+    first += __shfl(si, 63, 64);
+    prow += __shfl(sp, 63, 64);
+  }
+  return false;
+}
+
+// One work item: split it.k of row tile it.rt of one request.
+template <bool kArgmax>
+__device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, const Item &it) {
+  const Segment &seg = it.seg;
   const int H = a.H;
-  const int rows_req = seg.T * H;
-  const int row0 = tile * kRows;
-  if (row0 >= rows_req) return;
+  const int rows_req = it.rows;
+  const int row0 = it.rt * kRows;
 
   Ctx c;
   c.kv = static_cast<const uint16_t *>(a.kv);
@@ -600,15 +827,15 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   c.col = c.lane & 31;
   const int rho = row0 + c.wave * 32 + c.col;  // local row: token rho / H, head rho % H
   const bool row_ok = rho < rows_req;
+  // a wavefront past the request's rows only stages its share of each tile
+  const bool active = row0 + c.wave * 32 < rows_req;  // wave-uniform
   const int rho_c = row_ok ? rho : rows_req - 1;  // rows past the end compute, never write
   const int tok = rho_c / H;
   const int64_t grow = (seg.q0 + tok) * int64_t(H) + rho_c % H;
 
-  // this split's keys: whole tiles
-  const int per = (seg.L + S - 1) / S;
-  const int chunk = (per + kTK - 1) / kTK * kTK;
-  c.k0 = min(seg.L, s * chunk);
-  c.k1 = min(seg.L, c.k0 + chunk);
+  // this split's keys: whole tiles (k * ct < kt, so k0 < L)
+  c.k0 = it.k * it.ct * kTK;
+  c.k1 = int(min(int64_t(seg.L), int64_t(c.k0) + int64_t(it.ct) * kTK));
   const int ntiles = (c.k1 - c.k0 + kTK - 1) / kTK;
 
   const LaneOffs lo = lane_offsets(c);
@@ -628,7 +855,7 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   // query fragments (B operand): row `col`, dims 16*kc + 8*half .. +8; all requested now,
   // made opaque to the optimiser only after the tile loads are issued (below)
   u32x4 qv[kQFrags];
-  {
+  if (active) {
     const uint4 *qrow = reinterpret_cast<const uint4 *>(
         static_cast<const uint16_t *>(a.q) + grow * kDim);
 #pragma unroll
@@ -694,8 +921,12 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
       io.vwr = v0;
       io.dma_raw = 0;
       const f32x16 unused = {};
-      step<kFirst>(c, lo, io, none, slot_vec, 0, qf, o, scur, unused, st, c2, pf);
-      score_max<kArgmax>(c, c.k0, g_okbits[0], scur, o, st, c2, row_ok, mseg, moff);
+      if (active) {
+        step<kFirst>(c, lo, io, none, slot_vec, 0, qf, o, scur, unused, st, c2, pf);
+        score_max<kArgmax>(c, c.k0, g_okbits[0], scur, o, st, c2, row_ok, mseg, moff);
+      } else {
+        step<kFirst, false>(c, lo, io, none, slot_vec, 0, qf, o, scur, unused, st, c2, pf);
+      }
     }
     wait_tile_loads();
     __syncthreads();
@@ -713,10 +944,14 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
       sio.dma_raw = lds_addr(b ? raw1 : raw0);
       publish_ok(c, b, tl.ok);
       f32x16 snext;
-      step<kMain>(c, lo, sio, tl, slot_vec, t + 3, qf, o, snext, scur, st, c2, pf);
-      score_max<kArgmax>(c, c.k0 + (t + 1) * kTK, g_okbits[b ^ 1], snext, o, st, c2, row_ok,
-                         mseg, moff);
-      scur = snext;
+      if (active) {
+        step<kMain>(c, lo, sio, tl, slot_vec, t + 3, qf, o, snext, scur, st, c2, pf);
+        score_max<kArgmax>(c, c.k0 + (t + 1) * kTK, g_okbits[b ^ 1], snext, o, st, c2, row_ok,
+                           mseg, moff);
+        scur = snext;
+      } else {
+        step<kMain, false>(c, lo, sio, tl, slot_vec, t + 3, qf, o, snext, scur, st, c2, pf);
+      }
       wait_tile_loads();
       __syncthreads();
     }
@@ -728,14 +963,22 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
     eio.vwr = v0;
     eio.dma_raw = 0;
     f32x16 unused2;
-    step<kLast>(c, lo, eio, none, slot_vec, 0, qf, o, unused2, scur, st, c2, pf);
+    if (active) step<kLast>(c, lo, eio, none, slot_vec, 0, qf, o, unused2, scur, st, c2, pf);
   }
 
   // ---- write the partial of this split
+  if (!active) return;
   matrix_drain();
   const float ltot = st.lsum + swap_halves(st.lsum);
   if (!row_ok) return;
-  const int64_t prow = int64_t(s) * ws.rows_cap + grow;
+  const int64_t prow = it.prow + int64_t(it.k) * rows_req + rho;
+  if (it.k == 0 && c.half == 0) {
+    RowInfo ri;
+    ri.base = it.prow + rho;
+    ri.n = it.n;
+    ri.stride = rows_req;
+    ws.row_info[grow] = ri;
+  }
   float4 *po = reinterpret_cast<float4 *>(ws.part_o + prow * kLatent);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
 #pragma unroll
@@ -753,22 +996,313 @@ mfma_partial_kernel(RunArgs a, Workspace ws, int tiles_per_req, int n_work) {
   }
 }
 
+
+// ---- one work item of at most 32 rows: the four wavefronts share the rows and split the
+// work. Wavefront w computes the scores over dims [144w, 144w + 144) (9 fragments), the four
+// partial score tiles are summed through LDS in a fixed order (so every wavefront holds the
+// same scores and makes the same softmax decisions), and wavefront w accumulates output dims
+// [128w, 128w + 128). Per tile a wavefront issues 17 matrix instructions instead of 68, so a
+// workgroup streams key tiles about as fast as its loads arrive. Tiles are staged exactly as
+// in the 128-row path (same LDS layout, loads, fp16 conversion); the loads of tile t+2 are
+// issued as soon as every wavefront is done with tile t's raw buffer.
+constexpr int kNarrowFrags = kQFrags / kWaves;    // 9 score fragments per wavefront
+constexpr int kNarrowBlocks = kDBlocks / kWaves;  // 4 output dim blocks per wavefront
+
+// The slots of this wavefront's 8 rows of tile t into g_slots[t & 1][wave]: lane l < 16
+// loads dword l & 1 of row l >> 1's slot (keys past the split load a valid entry of the split
+// instead, and read_slots discards it). One load instruction per call.
+__device__ __forceinline__ void load_slots_lds(const Ctx &c, int t) {
+  if (c.lane < 2 * kRowsPerWave) {
+    const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane >> 1);
+    const int jc = min(j, c.k1 - 1);
+    const int64_t *e = (c.tree && jc >= c.P) ? c.tree + (jc - c.P) : c.kvi + jc;
+    dma_dword_lanes(reinterpret_cast<const uint32_t *>(e) + (c.lane & 1),
+                    lds_addr(reinterpret_cast<const char *>(&g_slots[t & 1][c.wave][0])));
+  }
+}
+// Lane l's slot of row l & 7 of tile t from g_slots (-1 past the split), once loaded.
+__device__ __forceinline__ int64_t read_slots(const Ctx &c, int t) {
+  const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane & 7);
+  // (a plain LDS read: the wait before it is an assembly statement with a memory clobber, so
+  // the read is not moved above it)
+  const int64_t v = g_slots[t & 1][c.wave][c.lane & 7];
+  return j < c.k1 ? v : -1;
+}
+
+template <bool kArgmax>
+__device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws,
+                                           const Item &it) {
+  const Segment &seg = it.seg;
+  const int H = a.H;
+  const int rows_req = it.rows;
+  const int row0 = it.rt * kRows;
+
+  Ctx c;
+  c.kv = static_cast<const uint16_t *>(a.kv);
+  c.kvi = a.kv_indices + seg.kv0;
+  c.tree = seg.tree;
+  c.zero = ws.zero_row;
+  c.num_slots = a.num_slots;
+  c.status = ws.status;
+  c.P = seg.P;
+  c.wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  c.lane = int(threadIdx.x) & 63;
+  c.half = c.lane >> 5;
+  c.col = c.lane & 31;
+  const int rho = row0 + c.col;  // every wavefront: the same 32 rows
+  const bool row_ok = rho < rows_req;
+  const int rho_c = row_ok ? rho : rows_req - 1;
+  const int tok = rho_c / H;
+  const int64_t grow = (seg.q0 + tok) * int64_t(H) + rho_c % H;
+
+  c.k0 = it.k * it.ct * kTK;
+  c.k1 = int(min(int64_t(seg.L), int64_t(c.k0) + int64_t(it.ct) * kTK));
+  const int ntiles = (c.k1 - c.k0 + kTK - 1) / kTK;
+
+  const LaneOffs lo = lane_offsets(c);
+  char *const raw0 = g_lds;
+  char *const raw1 = g_lds + kRawTile;
+  char *const v0 = g_lds + kVOff;
+  char *const v1 = g_lds + kVOff + kVTile;
+  float4 *const xbuf = reinterpret_cast<float4 *>(g_lds + kXOff);
+  const int kc0 = kNarrowFrags * c.wave;  // this wavefront's first score fragment
+
+  // ---- prologue (as in the 128-row path): slots of tiles 0 and 1, this wavefront's query
+  // fragments, the loads of tiles 0 and 1, the slots of tile 2
+  int64_t s0 = fetch_slot(c, 0);
+  int64_t s1 = fetch_slot(c, 1);
+  u32x4 qv[kNarrowFrags];
+  {
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(
+        static_cast<const uint16_t *>(a.q) + grow * kDim);
+#pragma unroll
+    for (int i = 0; i < kNarrowFrags; ++i)
+      qv[i] = __builtin_bit_cast(u32x4, qrow[2 * (kc0 + i) + c.half]);
+  }
+  // Key slots from tile 2 on travel through LDS (load_slots_lds / read_slots), loaded by one
+  // load instruction per tile whose completion the code tracks itself: every wait below is
+  // for a known number of newer loads (the compiler does not count these assembly loads, so a
+  // register result would be waited for with vmcnt(0), draining the tile loads behind it).
+  // Issue order per tile: its slots, then (a tile later) its 9 row loads.
+  {
+    const TileLoads t0 = plan_tile(c, 0, s0);
+    const TileLoads t1 = plan_tile(c, 1, s1);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, t0, lds_addr(raw0), i);
+    issue_rope(c, t0, lds_addr(raw0));
+    load_slots_lds(c, 2);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, t1, lds_addr(raw1), i);
+    issue_rope(c, t1, lds_addr(raw1));
+    publish_ok(c, 0, t0.ok);
+    publish_ok(c, 1, t1.ok);
+  }
+  bf16x8 qf[kNarrowFrags];
+#pragma unroll
+  for (int i = 0; i < kNarrowFrags; ++i) {
+    asm volatile("" : "+v"(qv[i]));
+    qf[i] = __builtin_bit_cast(bf16x8, qv[i]);
+  }
+  // operand offsets of this wavefront's score fragments (latent, or rope for kc >= 32)
+  uint32_t koff[kNarrowFrags];
+#pragma unroll
+  for (int i = 0; i < kNarrowFrags; ++i) {
+    const int kc = kc0 + i;
+    koff[i] = kc < kLatFrags ? lo.k_lat + 32 * kc : lo.k_rope + 256 * (kc - kLatFrags);
+  }
+
+  f32x16 o[kNarrowBlocks];
+#pragma unroll
+  for (int d = 0; d < kNarrowBlocks; ++d) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+    pin_agpr(o[d]);
+  }
+  RowState st;
+  st.m = -INFINITY;
+  st.mx = -INFINITY;
+  st.lsum = 0.f;
+  st.best_j = -1;
+  const float c2 = a.scale * kLog2e;
+  const uint8_t *mseg = a.mask + seg.m0;
+  const uint32_t moff = uint32_t(tok) * uint32_t(seg.L);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    const char *kraw = b ? raw1 : raw0;
+    char *vbuf = b ? v1 : v0;
+    // tile t (and q) landed: the slots of tile t+2 and the 9 loads of tile t+1 are newer
+    wait_loads_but_10();
+    __syncthreads();
+    const uint32_t ok_t = g_okbits[b];
+
+    // this wavefront's partial scores of tile t (two chains), with the fp16 copy of the
+    // units this thread loaded slotted between the matrix instructions
+    f32x16 sa, sb;
+    u32x4 craw[kRowsPerWave];
+    static_for<0, kNarrowFrags>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                                      kraw + koff[i]));
+      if constexpr (i == 0) {
+        const f32x16 zero = {};
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], zero, 0, 0, 0);
+      } else if constexpr (i == 1) {
+        const f32x16 zero = {};
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], zero, 0, 0, 0);
+      } else if constexpr (i & 1) {
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], sb, 0, 0, 0);
+      } else {
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], sa, 0, 0, 0);
+      }
+      if constexpr (i < kRowsPerWave)
+        craw[i] = *reinterpret_cast<const u32x4 *>(kraw + lo.cv_rd + kLatStride * i);
+      if constexpr (i >= 1 && i <= kRowsPerWave) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) craw[i - 1][q] = bf16pair_to_f16pair(craw[i - 1][q]);
+        *reinterpret_cast<u32x4 *>(vbuf + lo.cv_wr + kVRow * (i - 1)) = craw[i - 1];
+      }
+    });
+    f32x16 part;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part[e] = sa[e] + sb[e];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      xbuf[(c.wave * 4 + q) * 64 + c.lane] =
+          make_float4(part[4 * q], part[4 * q + 1], part[4 * q + 2], part[4 * q + 3]);
+    // every wavefront's partial scores are out, tile t's raw buffer is no longer read and its
+    // fp16 copy is complete
+    __syncthreads();
+
+    // the slots of tile t+3, then the loads of tile t+2 into tile t's raw buffer (zero rows
+    // past the split) once its slots, older than the 9 loads of tile t+1 and the slot load
+    // just issued, have landed
+    {
+      load_slots_lds(c, t + 3);
+      wait_loads_but_10();
+      const TileLoads tl = plan_tile(c, t + 2, read_slots(c, t + 2));
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, tl, lds_addr(kraw), i);
+      issue_rope(c, tl, lds_addr(kraw));
+      publish_ok(c, b, tl.ok);
+    }
+
+    // the scores: the four partials summed in wavefront order
+    f32x16 sc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 x = xbuf[q * 64 + c.lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        const float4 y = xbuf[(w * 4 + q) * 64 + c.lane];
+        x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      }
+      sc[4 * q] = x.x; sc[4 * q + 1] = x.y; sc[4 * q + 2] = x.z; sc[4 * q + 3] = x.w;
+    }
+    score_max<kArgmax, kNarrowBlocks>(c, c.k0 + t * kTK, ok_t, sc, o, st, c2, row_ok, mseg,
+                                      moff);
+    f16x8 pf[2];
+    const float negm = neg_max(st);
+#pragma unroll
+    for (int part_i = 0; part_i < 8; ++part_i) p_part(part_i, sc, c2, negm, st.lsum, pf);
+    // a matrix instruction that reads a VGPR written by VALU needs 2 wait states; the
+    // compiler does not see the assembly matrix instructions below as such
+    asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]));
+
+    // O[:, 128w .. 128w+128) += P V over the tile's 32 keys
+    const char *vtr = vbuf + lo.v_tr;
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+      for (int db = 0; db < kNarrowBlocks; ++db) {
+        const int d = kNarrowBlocks * c.wave + db;
+        u32x4 r;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const fp16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+              (lds_fp16x4 *)(vtr + (16 * ch + 8 * rr) * kVRow + 64 * d));
+          const u32x2 w2 = __builtin_bit_cast(u32x2, x);
+          r[2 * rr] = w2[0];
+          r[2 * rr + 1] = w2[1];
+        }
+        pv_mfma(o[db], r, pf[ch]);
+      }
+    }
+  }
+
+  // ---- write this wavefront's 128 dims of the split's partial (and, from wavefront 0, the
+  // row's scalars and placement)
+  matrix_drain();
+  const float ltot = st.lsum + swap_halves(st.lsum);
+  if (!row_ok) return;
+  const int64_t prow = it.prow + int64_t(it.k) * rows_req + rho;
+  float4 *po = reinterpret_cast<float4 *>(ws.part_o + prow * kLatent);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+#pragma unroll
+  for (int db = 0; db < kNarrowBlocks; ++db) {
+    const int d = kNarrowBlocks * c.wave + db;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+      po[(32 * d + 8 * gq + 4 * c.half) / 4] =
+          make_float4(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
+                      o[db][4 * gq + 3] * inv);
+  }
+  if (c.wave == 0 && c.half == 0) {
+    if (it.k == 0) {
+      RowInfo ri;
+      ri.base = it.prow + rho;
+      ri.n = it.n;
+      ri.stride = rows_req;
+      ws.row_info[grow] = ri;
+    }
+    const bool any = ltot > 0.f;
+    ws.part_lse[prow] = any ? (st.m + log2f(ltot)) * kLn2 : -INFINITY;
+    ws.part_max[prow] = any ? st.mx * kLn2 : -INFINITY;
+    ws.part_arg[prow] = any && kArgmax ? st.best_j : -1;
+  }
+}
+
+template <bool kArgmax>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+mfma_partial_kernel(RunArgs a, Workspace ws, int G) {
+  // XCD-aware mapping: the launch deals workgroups to the 8 XCDs in turn, so workgroup b
+  // takes item (b % 8) * (nb / 8) + b / 8: consecutive items share an XCD's L2
+  const int nb = gridDim.x;  // a multiple of 8, at least G and the batch's row tiles
+  const int lane = int(threadIdx.x) & 63;
+  const int64_t w = (int(blockIdx.x) & 7) * (nb >> 3) + (int(blockIdx.x) >> 3);
+  Item it;
+  {
+    const ReqWork mine = req_work(a, lane);
+    const WorkPlan plan = plan_work(a, mine, G, ws.splits, ws.status,
+                                    blockIdx.x == 0 && threadIdx.x < 64, lane);
+    if (w >= plan.items || !find_item<true>(a, mine, plan, w, lane, it)) return;
+  }
+  if (it.rows - it.rt * kRows <= 32)
+    run_narrow<kArgmax>(a, ws, it);
+  else
+    run_item<kArgmax>(a, ws, it);
+}
 }  // namespace
 
 hipError_t launch_mfma_partial(const RunArgs &a, const Workspace &ws, int rows_per_block,
-                               hipStream_t st) {
-  if (rows_per_block != kRows) return hipErrorInvalidValue;
+                               int work_items, hipStream_t st) {
+  if (rows_per_block != kRows || work_items <= 0) return hipErrorInvalidValue;
+  if (a.bs <= 0) return hipSuccess;
+  // one workgroup per item: with a fixed split count S there are at most S items per row
+  // tile; otherwise the plan makes at most work_items items, or one per row tile when the
+  // batch has more row tiles than that
   const int64_t tiles = (int64_t(a.max_q_per_req) * a.H + kRows - 1) / kRows;
-  const int64_t n_work = int64_t(a.bs) * ws.splits * tiles;
-  if (n_work <= 0) return hipSuccess;
-  const int64_t nb = (n_work + 7) / 8 * 8;
+  const int64_t per_tile = ws.splits > 0 ? ws.splits : 1;
+  int64_t nb = std::max(int64_t(work_items), int64_t(a.bs) * tiles * per_tile);
+  nb = (nb + 7) / 8 * 8;
   if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.want_argmax)
     hipLaunchKernelGGL(mfma_partial_kernel<true>, dim3(unsigned(nb)), dim3(kThreads), 0, st, a,
-                       ws, int(tiles), int(n_work));
+                       ws, work_items);
   else
     hipLaunchKernelGGL(mfma_partial_kernel<false>, dim3(unsigned(nb)), dim3(kThreads), 0, st, a,
-                       ws, int(tiles), int(n_work));
+                       ws, work_items);
   return hipGetLastError();
 }
 

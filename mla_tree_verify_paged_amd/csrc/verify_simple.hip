@@ -171,7 +171,19 @@ simple_partial_kernel(RunArgs a, Workspace ws) {
   }
 
   if (!head_ok) return;
-  const int64_t prow = int64_t(s) * ws.rows_cap + row;
+  // request r's partials: S blocks of its R = T*H rows, after the S * q0 * H rows of the
+  // requests before it
+  const int64_t R = int64_t(seg.T) * a.H;
+  const int64_t x = row - seg.q0 * a.H;
+  const int64_t base = int64_t(S) * seg.q0 * a.H + x;
+  const int64_t prow = base + int64_t(s) * R;
+  if (s == 0 && lane == 0) {
+    RowInfo ri;
+    ri.base = base;
+    ri.n = S;
+    ri.stride = int32_t(R);
+    ws.row_info[row] = ri;
+  }
   float *po = ws.part_o + prow * kLatent;
   if (l > 0.f) {
     const float inv = 1.f / l;

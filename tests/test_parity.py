@@ -159,3 +159,60 @@ def test_mfma_matches_simple_closely():
     a = run_gpu(w, kernel="simple")
     b = run_gpu(w, kernel="mfma")
     assert np.max(np.abs(a[0] - b[0])) <= 5e-3
+
+
+# ----------------------------------------------------------------------------- few rows per request
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_tp8_full(kernel):
+    """H=8, T=4: 32 rows against 23,004 keys (three of the four wavefronts have no rows)."""
+    w = wl.tp8()
+    say(f"tp8, {kernel}")
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_tp8_batch_sampled(kernel):
+    w = wl.tp8_batch()
+    rows = sample_rows(w, 256, seed=3)
+    say(f"tp8_batch, {kernel}, {len(rows)} sampled rows")
+    ref = run_oracle(w, rows=rows)
+    compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
+
+
+# ----------------------------------------------------------------------------- the device work list
+def test_work_list_more_requests_than_a_wavefront():
+    """70 requests of mixed length: the plan scans the request tables in chunks of 64, and the
+    long requests get several splits while the short ones get one."""
+    rng = np.random.default_rng(15)
+    p = np.where(rng.random(70) < 0.1, rng.integers(3000, 9000, 70), rng.integers(0, 400, 70))
+    t = rng.integers(1, 5, 70)
+    w = wl.build_workload("wl70", rng, 8, p, t, int((p + t).sum()) * 2)
+    say(f"work list: bs=70 H=8 sum P={int(p.sum())}")
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel="mfma"), ref)
+    # a context sized for more requests than the call has
+    compare(w, run_gpu(w, kernel="mfma", max_batch=130, max_q_per_req=9), ref)
+
+
+def test_work_list_more_row_tiles_than_workgroups():
+    """300 requests x 2 row tiles: more row tiles than compute units, so each row tile is one
+    item covering all of its request's keys."""
+    rng = np.random.default_rng(16)
+    p = rng.integers(0, 200, 300)
+    t = rng.integers(3, 5, 300)
+    w = wl.build_workload("wl300", rng, 64, p, t, int((p + t).sum()) * 2)
+    rows = sample_rows(w, 2048, seed=4)
+    say(f"work list: bs=300 H=64, {len(rows)} sampled rows")
+    ref = run_oracle(w, rows=rows)
+    compare(w, run_gpu(w, kernel="mfma"), ref, rows=rows)
+
+
+def test_work_list_one_long_request_among_short_ones():
+    rng = np.random.default_rng(17)
+    w = wl.build_workload("wl_skew", rng, 64, [40000, 100, 0, 2500], [16, 3, 7, 1], 1 << 17)
+    rows = sample_rows(w, 512, seed=5)
+    say(f"work list: skewed batch, {len(rows)} sampled rows")
+    ref = run_oracle(w, rows=rows)
+    compare(w, run_gpu(w, kernel="mfma"), ref, rows=rows)
+    compare(w, run_gpu(w, kernel="mfma", num_splits=7), ref, rows=rows)
