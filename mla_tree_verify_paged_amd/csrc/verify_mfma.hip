@@ -557,28 +557,28 @@ __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits,
   }
   // max of the raw scores (the scale is positive, so it keeps the order), then the lane
   // pair holding the other 16 keys of the row
-  float tmax;
-  int targ = 0x7fffffff;
+  float tmax = sacc[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
+  tmax = fmaxf(tmax, other_half(tmax));
+  const float tmax2 = tmax * c2;  // log2 units
   if (kArgmax) {
-    tmax = -INFINITY;
+    // the argmax moves only when the row's max grows, which soon becomes rare: locate it only
+    // then (the lowest key position holding the tile max, over both lane halves)
+    const bool improve = tmax2 > st.mx;
+    if (__any(improve)) {
+      int targ = 0x7fffffff;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kk = 8 * (e >> 2) + 4 * c.half + (e & 3);
-      if (sacc[e] > tmax) { tmax = sacc[e]; targ = kb + kk; }
+      for (int e = 15; e >= 0; --e) {
+        const int kk = 8 * (e >> 2) + 4 * c.half + (e & 3);
+        if (sacc[e] == tmax) targ = kb + kk;
+      }
+      targ = min(targ, other_half(targ));
+      if (improve) st.best_j = targ;
     }
-    const float om = other_half(tmax);
-    const int oj = other_half(targ);
-    if (om > tmax || (om == tmax && oj < targ)) targ = oj;
-    tmax = fmaxf(tmax, om);
-  } else {
-    tmax = sacc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, sacc[e]);
-    tmax = fmaxf(tmax, other_half(tmax));
   }
-  tmax *= c2;  // log2 units
-  if (kArgmax && tmax > st.mx) st.best_j = targ;
-  st.mx = fmaxf(st.mx, tmax);
+  st.mx = fmaxf(st.mx, tmax2);
+  tmax = tmax2;
 
   // lazy rescale of the running max (rare after the first tile)
   const bool need = tmax > st.m + kRescale;
