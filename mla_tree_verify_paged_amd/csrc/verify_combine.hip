@@ -11,8 +11,8 @@
 // One workgroup per row. Every wavefront reads the per-split scalars lane-parallel (lane s
 // holds split s) and derives the same max, weights and argmax; the splits' partial rows are
 // dealt to the four wavefronts (split s to wavefront s % 4), each lane owning 8 output dims,
-// with up to 8 splits' rows in flight per wavefront; the four partial sums meet in LDS. A row
-// with many splits (few rows, long keys) is thus read by 256 threads. The combine also owns
+// with 4 (8 when the step has few rows) splits' rows in flight per wavefront; the four partial
+// sums meet in LDS. A row with many splits (few rows, long keys) is thus read by 256 threads. The combine also owns
 // output validation: a row whose token belongs to no valid request is written empty (out 0,
 // lse -inf, argmax -1) and the matching status bit is set, so every output element is defined
 // whatever the device-side tables hold.
@@ -25,7 +25,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBatch = 8;  // splits whose rows a wavefront has in flight
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -64,6 +63,9 @@ __device__ __forceinline__ void fma8(float4 &lo, float4 &hi, float w, const floa
   hi.z = fmaf(w, x1.z, hi.z); hi.w = fmaf(w, x1.w, hi.w);
 }
 
+// kBatch: splits whose rows a wavefront has in flight. Fewer keep more workgroups resident
+// (4 when the step has many rows), more shorten a row with many splits (8 for few rows).
+template <int kBatch>
 __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace ws) {
   __shared__ float4 red[kWaves - 1][kLatent / 4];
   const int lane = threadIdx.x & 63;
@@ -216,7 +218,10 @@ hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st)
   const int64_t rows = a.num_tokens * a.H;
   if (rows <= 0) return hipSuccess;
   if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(rows)), dim3(kThreads), 0, st, a, ws);
+  if (rows < 512)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(unsigned(rows)), dim3(kThreads), 0, st, a, ws);
+  else
+    hipLaunchKernelGGL(combine_kernel<4>, dim3(unsigned(rows)), dim3(kThreads), 0, st, a, ws);
   return hipGetLastError();
 }
 
