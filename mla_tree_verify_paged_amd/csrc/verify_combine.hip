@@ -65,13 +65,35 @@ __device__ __forceinline__ void fma8(float4 &lo, float4 &hi, float w, const floa
 
 // kBatch: splits whose rows a wavefront has in flight. Fewer keep more workgroups resident
 // (4 when the step has many rows), more shorten a row with many splits (8 for few rows).
-template <int kBatch>
+// the 2 output dims [dim0, dim0 + 2) of `row`
+__device__ void store2(const RunArgs &a, int64_t row, int dim0, float x, float y) {
+  if (a.out_bf16) {
+    *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + row * kLatent + dim0) =
+        f32_to_bf16_rne(x) | (f32_to_bf16_rne(y) << 16);
+  } else {
+    *reinterpret_cast<float2 *>(static_cast<float *>(a.out) + row * kLatent + dim0) =
+        make_float2(x, y);
+  }
+}
+
+// One workgroup per (row, dim slice). kSlices = 1: the whole 512-dim row, each lane owning 8
+// dims ([4l, 4l+4) and [256+4l, 256+4l+4)); kSlices = 4 (steps with few rows, whose rows have
+// many splits): a quarter of the row per workgroup, each lane owning 2 dims, so a row's
+// splits are read by four workgroups on four compute units. kBatch: splits whose slices a
+// wavefront has in flight (fewer keep more workgroups resident).
+template <int kBatch, int kSlices>
 __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace ws) {
-  __shared__ float4 red[kWaves - 1][kLatent / 4];
+  constexpr int kV = 8 / kSlices;           // dims per lane
+  constexpr int kSliceDims = kLatent / kSlices;
+  __shared__ float red[kWaves - 1][kV][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t row = blockIdx.x;
+  const int64_t row = blockIdx.x / kSlices;
+  const int slice = int(blockIdx.x % kSlices);
   const int64_t t = row / a.H;
+  // the lane's dims: kV consecutive ones at dim_a (kSlices > 1), or 4 at dim_a and 4 at
+  // dim_a + 256
+  const int dim_a = kSlices == 1 ? 4 * lane : slice * kSliceDims + kV * lane;
 
   // where this row's partials are (written by the partial kernel for every row of a valid
   // request; for other rows it is stale or arbitrary, so it is only used once checked to stay
@@ -88,24 +110,49 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   }
   const float *plse = ws.part_lse + base;
   const float *pmax = ws.part_max + base;
-  // lane l holds 8 dims: [4l, 4l + 4) and [256 + 4l, 256 + 4l + 4)
-  const float *po = ws.part_o + base * kLatent + 4 * lane;
+  const float *po = ws.part_o + base * kLatent + dim_a;
   const int64_t ostride = stride * kLatent;
+  auto load = [&](int sp, float *x) __attribute__((always_inline)) {
+    const float *src = po + sp * ostride;
+    if constexpr (kSlices == 1) {
+      const float4 u = *reinterpret_cast<const float4 *>(src);
+      const float4 v = *reinterpret_cast<const float4 *>(src + 256);
+      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+      x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    } else {
+      static_assert(kV == 2, "two dims per lane");
+      const float2 u = *reinterpret_cast<const float2 *>(src);
+      x[0] = u.x; x[1] = u.y;
+    }
+  };
+  auto store = [&](const float *v) __attribute__((always_inline)) {
+    if constexpr (kSlices == 1) {
+      store4(a, row, dim_a, make_float4(v[0], v[1], v[2], v[3]));
+      store4(a, row, dim_a + 256, make_float4(v[4], v[5], v[6], v[7]));
+    } else {
+      store2(a, row, dim_a, v[0], v[1]);
+    }
+  };
 
   // Requested before the row is validated, so that one memory round trip serves all of them:
   // this wavefront's first kBatch splits and the scalars of the first 64 (all inside the
   // workspace, as checked above).
-  float4 x0[kBatch], x1[kBatch];
+  float x[kBatch][kV];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
     const int sp = wave + kWaves * j;
-    if (sp < S) {
-      x0[j] = *reinterpret_cast<const float4 *>(po + sp * ostride);
-      x1[j] = *reinterpret_cast<const float4 *>(po + sp * ostride + 256);
-    }
+    if (sp < S) load(sp, x[j]);
   }
-  const float lse0 = lane < S ? plse[int64_t(lane) * stride] : -INFINITY;
-  const float max0 = lane < S ? pmax[int64_t(lane) * stride] : -INFINITY;
+  // the scalars of splits lane + 64*i, i < kScal (kSlices > 1: rows with many splits read all
+  // of them in this one round trip; otherwise only the first 64 here)
+  constexpr int kScal = kSlices > 1 ? 4 : 1;
+  float lsv[kScal], mxv[kScal];
+#pragma unroll
+  for (int i = 0; i < kScal; ++i) {
+    const int sp = lane + 64 * i;
+    lsv[i] = sp < S ? plse[int64_t(sp) * stride] : -INFINITY;
+    mxv[i] = sp < S ? pmax[int64_t(sp) * stride] : -INFINITY;
+  }
 
   // the request that owns token t: the last r with qo_indptr[r] <= t
   uint32_t bad = 0;
@@ -128,19 +175,27 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
     bad = 8u;
   }
   if (!ok) {
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && slice == 0) {
       atomicOr(ws.status, bad);
       if (a.out_lse) a.out_lse[row] = -INFINITY;
       if (a.out_argmax) a.out_argmax[row] = -1;
     }
-    if (threadIdx.x < kLatent / 4) store4(a, row, 4 * threadIdx.x, make_float4(0.f, 0.f, 0.f, 0.f));
+    if (wave == 0) {
+      const float zero[kV] = {};
+      store(zero);
+    }
     return;
   }
 
   // per-split scalars, lane-parallel (lane s holds split s, then s + 64, ...); every
   // wavefront computes the same M, best and W
-  float M = lse0, best = max0;
-  for (int s0 = 64; s0 < S; s0 += 64) {
+  float M = lsv[0], best = mxv[0];
+#pragma unroll
+  for (int i = 1; i < kScal; ++i) {
+    M = fmaxf(M, lsv[i]);
+    best = fmaxf(best, mxv[i]);
+  }
+  for (int s0 = 64 * kScal; s0 < S; s0 += 64) {
     const int s = s0 + lane;
     if (s < S) {
       M = fmaxf(M, plse[int64_t(s) * stride]);
@@ -152,16 +207,28 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
 
   float W = 0.f;
   int arg = -1;
-  float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
+  float acc[kV];
+#pragma unroll
+  for (int e = 0; e < kV; ++e) acc[e] = 0.f;
   if (M != -INFINITY) {
     for (int s0 = 0; s0 < S; s0 += 64) {
       const int s = s0 + lane;
-      const float ls = s < 64 ? (s < S ? lse0 : -INFINITY)
-                              : (s < S ? plse[int64_t(s) * stride] : -INFINITY);
+      // the scalars of split s: held since the first round trip, or read now
+      float ls = -INFINITY, mx = -INFINITY;
+      if (s0 < 64 * kScal) {
+#pragma unroll
+        for (int i = 0; i < kScal; ++i)
+          if (s0 == 64 * i) {
+            ls = lsv[i];
+            mx = mxv[i];
+          }
+      } else if (s < S) {
+        ls = plse[int64_t(s) * stride];
+        mx = pmax[int64_t(s) * stride];
+      }
       const float wgt = ls == -INFINITY ? 0.f : expf(ls - M);
       W += wave_sum(wgt);
       if (arg < 0) {  // wave-uniform: the lowest split holding the largest max score
-        const float mx = s < 64 ? max0 : (s < S ? pmax[int64_t(s) * stride] : -INFINITY);
         const uint64_t hit = __ballot(s < S && mx == best);
         if (hit) arg = ws.part_arg[base + int64_t(s0 + __builtin_ctzll(hit)) * stride];
       }
@@ -172,10 +239,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
 #pragma unroll
           for (int j = 0; j < kBatch; ++j) {
             const int sp = s0 + wave + kWaves * (j0 + j);
-            if (sp < S) {
-              x0[j] = *reinterpret_cast<const float4 *>(po + sp * ostride);
-              x1[j] = *reinterpret_cast<const float4 *>(po + sp * ostride + 256);
-            }
+            if (sp < S) load(sp, x[j]);
           }
         }
 #pragma unroll
@@ -183,30 +247,31 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
           const int sl = wave + kWaves * (j0 + j);  // lane of this split within the 64
           const float wk = __shfl(wgt, sl, 64);
           // a split with zero weight contributes nothing (its row may be unwritten)
-          if (s0 + sl < S && wk != 0.f) fma8(acc0, acc1, wk, x0[j], x1[j]);
+          if (s0 + sl < S && wk != 0.f) {
+#pragma unroll
+            for (int e = 0; e < kV; ++e) acc[e] = fmaf(wk, x[j][e], acc[e]);
+          }
         }
       }
     }
   }
   // the four wavefronts' sums meet in LDS; wavefront 0 finishes the row
   if (wave > 0) {
-    red[wave - 1][lane] = acc0;
-    red[wave - 1][64 + lane] = acc1;
+#pragma unroll
+    for (int e = 0; e < kV; ++e) red[wave - 1][e][lane] = acc[e];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int k = 0; k < kWaves - 1; ++k) {
-    const float4 r0 = red[k][lane], r1 = red[k][64 + lane];
-    acc0.x += r0.x; acc0.y += r0.y; acc0.z += r0.z; acc0.w += r0.w;
-    acc1.x += r1.x; acc1.y += r1.y; acc1.z += r1.z; acc1.w += r1.w;
+#pragma unroll
+    for (int e = 0; e < kV; ++e) acc[e] += red[k][e][lane];
   }
   const float inv = M == -INFINITY ? 0.f : 1.f / W;
-  acc0.x *= inv; acc0.y *= inv; acc0.z *= inv; acc0.w *= inv;
-  acc1.x *= inv; acc1.y *= inv; acc1.z *= inv; acc1.w *= inv;
-  store4(a, row, 4 * lane, acc0);
-  store4(a, row, 256 + 4 * lane, acc1);
-  if (lane == 0) {
+#pragma unroll
+  for (int e = 0; e < kV; ++e) acc[e] *= inv;
+  store(acc);
+  if (lane == 0 && slice == 0) {
     if (a.out_lse) a.out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
     if (a.out_argmax) a.out_argmax[row] = arg;
   }
@@ -218,10 +283,15 @@ hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st)
   const int64_t rows = a.num_tokens * a.H;
   if (rows <= 0) return hipSuccess;
   if (rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (rows < 512)
-    hipLaunchKernelGGL(combine_kernel<8>, dim3(unsigned(rows)), dim3(kThreads), 0, st, a, ws);
-  else
-    hipLaunchKernelGGL(combine_kernel<4>, dim3(unsigned(rows)), dim3(kThreads), 0, st, a, ws);
+  if (rows < 512) {
+    // few rows: a quarter of a row per workgroup
+    if (rows * 4 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((combine_kernel<16, 4>), dim3(unsigned(rows * 4)), dim3(kThreads), 0, st,
+                       a, ws);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<4, 1>), dim3(unsigned(rows)), dim3(kThreads), 0, st, a,
+                       ws);
+  }
   return hipGetLastError();
 }
 
