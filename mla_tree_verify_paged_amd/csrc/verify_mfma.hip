@@ -1136,14 +1136,21 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
     __syncthreads();
     const uint32_t ok_t = g_okbits[b];
 
-    // this wavefront's partial scores of tile t (two chains), with the fp16 copy of the
-    // units this thread loaded slotted between the matrix instructions
+    // this wavefront's partial scores of tile t (two chains) and the fp16 copy of the units
+    // this thread loaded. Every LDS read of the phase is issued first: the assembly matrix
+    // instructions end the compiler's scheduling regions, so reads placed between them would
+    // each wait out a full LDS round trip.
+    u32x4 kf[kNarrowFrags], craw[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kNarrowFrags; ++i)
+      kf[i] = *reinterpret_cast<const u32x4 *>(kraw + koff[i]);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i)
+      craw[i] = *reinterpret_cast<const u32x4 *>(kraw + lo.cv_rd + kLatStride * i);
     f32x16 sa, sb;
-    u32x4 craw[kRowsPerWave];
     static_for<0, kNarrowFrags>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                                                      kraw + koff[i]));
+      const bf16x8 av = __builtin_bit_cast(bf16x8, kf[i]);
       if constexpr (i == 0) {
         const f32x16 zero = {};
         sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], zero, 0, 0, 0);
@@ -1155,14 +1162,13 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
       } else {
         sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], sa, 0, 0, 0);
       }
-      if constexpr (i < kRowsPerWave)
-        craw[i] = *reinterpret_cast<const u32x4 *>(kraw + lo.cv_rd + kLatStride * i);
-      if constexpr (i >= 1 && i <= kRowsPerWave) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) craw[i - 1][q] = bf16pair_to_f16pair(craw[i - 1][q]);
-        *reinterpret_cast<u32x4 *>(vbuf + lo.cv_wr + kVRow * (i - 1)) = craw[i - 1];
-      }
     });
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) craw[i][q] = bf16pair_to_f16pair(craw[i][q]);
+      *reinterpret_cast<u32x4 *>(vbuf + lo.cv_wr + kVRow * i) = craw[i];
+    }
     f32x16 part;
 #pragma unroll
     for (int e = 0; e < 16; ++e) part[e] = sa[e] + sb[e];
@@ -1209,24 +1215,28 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
     // compiler does not see the assembly matrix instructions below as such
     asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]));
 
-    // O[:, 128w .. 128w+128) += P V over the tile's 32 keys
+    // O[:, 128w .. 128w+128) += P V over the tile's 32 keys (all V^T reads first, as above)
     const char *vtr = vbuf + lo.v_tr;
+    u32x4 vf[2][kNarrowBlocks];
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
       for (int db = 0; db < kNarrowBlocks; ++db) {
         const int d = kNarrowBlocks * c.wave + db;
-        u32x4 r;
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
           const fp16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
               (lds_fp16x4 *)(vtr + (16 * ch + 8 * rr) * kVRow + 64 * d));
           const u32x2 w2 = __builtin_bit_cast(u32x2, x);
-          r[2 * rr] = w2[0];
-          r[2 * rr + 1] = w2[1];
+          vf[ch][db][2 * rr] = w2[0];
+          vf[ch][db][2 * rr + 1] = w2[1];
         }
-        pv_mfma(o[db], r, pf[ch]);
       }
+    }
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+      for (int db = 0; db < kNarrowBlocks; ++db) pv_mfma(o[db], vf[ch][db], pf[ch]);
     }
   }
 
