@@ -308,11 +308,12 @@ struct RowState {
 // A step issues the 68 matrix instructions of one tile's worth of work in a fixed order
 // (written as a table), and slots the vector work between them:
 //  kFirst - QK^T of tile 0 (36 instructions) and the fp16 copy of tile 0;
-//  kMain  - phase A: exp/round/sum of P(t) interleaved with QK^T fragments 0..11 of tile t+1;
-//           phase B: P(t).V(t) interleaved with QK^T fragments 12..35 of tile t+1, the fp16
-//           copy of tile t+1, the loads of tile t+2 and the slot fetch of tile t+3; the last
-//           eight P.V products cover the latency of the final QK^T result and the merge of
-//           the two score chains;
+//  kMain  - phase A: exp/round/sum of P(t) interleaved with QK^T fragments 0..11 of tile t+1,
+//           and the loads of tile t+2 (one row every second op from op 1) and the slot fetch
+//           of tile t+3;
+//           phase B: P(t).V(t) interleaved with QK^T fragments 12..35 of tile t+1 and the fp16
+//           copy of tile t+1; the last eight P.V products cover the latency of the final
+//           QK^T result and the merge of the two score chains;
 //  kLast  - exp/round/sum of P(t), then P(t).V(t).
 // QK^T fragments alternate between two accumulation chains (even and odd fragments), so a
 // matrix instruction never waits on the one just before it.
@@ -352,8 +353,12 @@ template <> struct StepPlan<kMain> {
     return t;
   }
   static constexpr int rd(int u) { return kPhaseA + 2 + 6 * u; }
-  static constexpr int kDmaOp = kPhaseA + 1;    // loads of tile t+2 after ops 13..21
-  static constexpr int kSlotOp = kDmaOp + 9;    // slot fetch of tile t+3 after op 22
+  // the loads of tile t+2: one row after every second op from op 1 (rows 0..7 after ops
+  // 1, 3, .., 15, the rope block after op 17), so that the four wavefronts' 36 loads reach
+  // the address unit spread out rather than back to back; then the slots of tile t+3
+  static constexpr int kDmaOp = 1;
+  static constexpr int kDmaStride = 2;
+  static constexpr int kSlotOp = kDmaOp + kDmaStride * kRowsPerWave + 1;
   static constexpr int kMergeOp = kOps - 7;     // chain merge after ops 61..67
 };
 template <> struct StepPlan<kLast> {
@@ -486,7 +491,8 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
     if constexpr (K == kMain && kCompute && p < 8) p_part(p, scur, c2, negm, st.lsum, pf);
     // the loads of tile t+2 (zero rows past the split), then the slots of tile t+3
     if constexpr (K == kMain) {
-      constexpr int dp = p - Plan::kDmaOp;
+      constexpr int dq = p - Plan::kDmaOp;
+      constexpr int dp = (dq >= 0 && dq % Plan::kDmaStride == 0) ? dq / Plan::kDmaStride : -1;
       if constexpr (dp >= 0 && dp < kRowsPerWave) issue_latent(c, tl, io.dma_raw, dp);
       if constexpr (dp == kRowsPerWave) issue_rope(c, tl, io.dma_raw);
       if constexpr (p == Plan::kSlotOp) slot_vec = fetch_slot(c, slot_tile);
