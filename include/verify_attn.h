@@ -106,7 +106,12 @@ typedef struct {
   int32_t max_batch;      /* upper bound on bs                                             */
   int32_t max_q_per_req;  /* upper bound on T_r                                            */
   int64_t max_q_tokens;   /* upper bound on num_tokens                                     */
-  int32_t num_splits;     /* key splits per request (1..256); 0 = chosen from the bounds    */
+  int32_t num_splits;     /* key splits per request (1..256): each request's keys are cut
+                             into that many splits (fewer if it has fewer 32-key tiles);
+                             0 = MFMA kernel: chosen on the device at every call, one common
+                             split length for the whole batch so that it has at most one work
+                             item per compute unit (one per row tile when the batch has more
+                             row tiles than that); simple kernel: chosen from the bounds     */
   int32_t kernel;         /* VA_KERNEL_*                                                   */
   void *workspace;        /* device memory, 256-byte aligned, or NULL: allocated at create.
                              Owned by the context until verify_attn_destroy: the caller must
@@ -116,13 +121,17 @@ typedef struct {
 
 typedef struct {
   int32_t kernel;         /* the kernel family actually used                              */
-  int32_t num_splits;     /* the split count fixed for the context's life                 */
+  int32_t num_splits;     /* the split count fixed for the context's life; 0 when the MFMA
+                             kernel balances the splits on the device at every call         */
   int32_t rows_per_block; /* (token, head) rows handled by one partial workgroup           */
-  int32_t row_tiles_per_req; /* row tiles per request in the launch grid                   */
+  int32_t row_tiles_per_req; /* row tiles a request can have (ceil(max_q_per_req*H / rows)) */
   size_t workspace_bytes; /* bytes of workspace in use                                     */
 } verify_attn_info;
 
-/* Workspace bytes a config needs (0 if the config is invalid). */
+/* Workspace bytes a config needs (0 if the config is invalid): about 2060 bytes per partial
+ * row, with (128 * CUs + max_q_tokens * H) partial rows for the MFMA kernel with
+ * num_splits = 0 (CUs = the current device's compute units, 256 when no device answers) and
+ * num_splits * max_q_tokens * H otherwise, plus 16 bytes per output row. */
 size_t verify_attn_workspace_bytes(const verify_attn_config *cfg);
 
 /* Validates `cfg`, binds or allocates the workspace, clears its status words and a row of
