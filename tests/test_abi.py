@@ -74,6 +74,32 @@ def test_workspace_bytes_positive_and_monotone_in_splits():
     assert b >= 8 * 1024 * 515 * 4
 
 
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+def _layout_bytes(part_rows, rows):
+    """The workspace layout the header documents: header, part_o, lse, max, arg, row_info."""
+    o = _align256(256 + 1152)
+    o = _align256(o + part_rows * 512 * 4)
+    for _ in range(3):
+        o = _align256(o + part_rows * 4)
+    return _align256(o + rows * 16)
+
+
+def test_workspace_size_follows_the_documented_layout():
+    rows = 16 * 64
+    # MFMA kernel, splits chosen on the device: 128 rows per item, one item per compute unit
+    # (256 when no device answers, as in this container), plus one row per output row
+    auto = B.verify_attn_workspace_bytes(cfg(kernel=B.VA_KERNEL_MFMA))
+    assert auto == _layout_bytes(128 * 256 + rows, rows)
+    # a fixed split count: that many partial rows per output row
+    assert B.verify_attn_workspace_bytes(cfg(kernel=B.VA_KERNEL_MFMA, num_splits=5)) == \
+        _layout_bytes(5 * rows, rows)
+    assert B.verify_attn_workspace_bytes(cfg(kernel=B.VA_KERNEL_SIMPLE, num_splits=3)) == \
+        _layout_bytes(3 * rows, rows)
+
+
 @pytest.mark.parametrize("bad", [
     dict(num_heads=0), dict(latent_dim=256), dict(rope_dim=0), dict(in_dtype=7),
     dict(out_dtype=3), dict(max_batch=0), dict(max_q_per_req=0), dict(num_splits=-1),
