@@ -691,6 +691,12 @@ __device__ __forceinline__ ReqWork chunk_request(const RunArgs &a, const ReqWork
 
 __device__ int64_t count_items(const RunArgs &a, const ReqWork &mine, int c, int forced,
                                int lane) {
+  if (a.bs == 1) {  // one request (lane 0's): no cross-lane sum
+    ReqWork q = mine;
+    q.rt = uniform(q.rt);
+    q.kt = uniform(q.kt);
+    return int64_t(q.rt) * split_count(q, c, forced);
+  }
   int64_t n = 0;
   for (int base = 0; base < a.bs; base += 64) {
     const ReqWork q = chunk_request<true>(a, mine, base, lane);
@@ -706,16 +712,24 @@ __device__ WorkPlan plan_work(const RunArgs &a, const ReqWork &mine, int G, int 
   p.forced = forced;
   int64_t C = 0, RT = 0;
   int ktmax = 0;
-  for (int base = 0; base < a.bs; base += 64) {
-    const ReqWork q = chunk_request<true>(a, mine, base, lane);
-    if (report && q.bad) atomicOr(status, q.bad);
-    C += wave_sum64(int64_t(q.rt) * q.kt);
-    RT += wave_sum64(int64_t(q.rt));
-    ktmax = max(ktmax, wave_max_int(q.kt));
+  if (a.bs == 1) {  // one request (lane 0's): no cross-lane sums
+    if (report && lane == 0 && mine.bad) atomicOr(status, mine.bad);
+    const int rt = uniform(mine.rt), kt = uniform(mine.kt);
+    C = int64_t(rt) * kt;
+    RT = rt;
+    ktmax = kt;
+  } else {
+    for (int base = 0; base < a.bs; base += 64) {
+      const ReqWork q = chunk_request<true>(a, mine, base, lane);
+      if (report && q.bad) atomicOr(status, q.bad);
+      C += wave_sum64(int64_t(q.rt) * q.kt);
+      RT += wave_sum64(int64_t(q.rt));
+      ktmax = max(ktmax, wave_max_int(q.kt));
+    }
+    C = uniform(C);
+    RT = uniform(RT);
+    ktmax = uniform(ktmax);
   }
-  C = uniform(C);
-  RT = uniform(RT);
-  ktmax = uniform(ktmax);
   if (forced > 0 || C == 0) {
     p.items = C == 0 ? 0 : count_items(a, mine, 1, forced, lane);
     return p;
@@ -764,6 +778,23 @@ __device__ __forceinline__ Segment uniform(const Segment &s) {
 template <bool kCached>
 __device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan &p, int64_t w,
                           int lane, Item &it) {
+  if (kCached && a.bs == 1) {  // one request (lane 0's): item w is its split w / rt, tile w % rt
+    ReqWork q = mine;
+    q.rows = uniform(q.rows);
+    q.rt = uniform(q.rt);
+    q.kt = uniform(q.kt);
+    const int n = split_count(q, p.c, p.forced);
+    if (q.rt == 0 || w >= int64_t(q.rt) * n) return false;
+    it.seg = uniform(q.seg);
+    it.seg.tree = a.out_cache_loc ? a.out_cache_loc + it.seg.q0 : nullptr;
+    it.rows = q.rows;
+    it.rt = int(w % q.rt);
+    it.k = int(w / q.rt);
+    it.n = n;
+    it.ct = split_tiles(q.kt, p.c, p.forced);
+    it.prow = 0;
+    return true;
+  }
   int64_t first = 0, prow = 0;
   for (int base = 0; base < a.bs; base += 64) {
     const ReqWork q = chunk_request<kCached>(a, mine, base, lane);
