@@ -1199,13 +1199,15 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
       } else {
         sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], sa, 0, 0, 0);
       }
+      // the fp16 copy of one unit after each matrix instruction, so that the conversion
+      // work issues while the matrix core runs
+      if constexpr (i < kRowsPerWave) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) craw[i][q] = bf16pair_to_f16pair(craw[i][q]);
+        *reinterpret_cast<u32x4 *>(vbuf + lo.cv_wr + kVRow * i) = craw[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     });
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) craw[i][q] = bf16pair_to_f16pair(craw[i][q]);
-      *reinterpret_cast<u32x4 *>(vbuf + lo.cv_wr + kVRow * i) = craw[i];
-    }
     f32x16 part;
 #pragma unroll
     for (int e = 0; e < 16; ++e) part[e] = sa[e] + sb[e];
@@ -1217,6 +1219,12 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
     // fp16 copy is complete
     __syncthreads();
 
+    // the four partial scores, requested before the loads below are issued
+    float4 xs[4][kWaves];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) xs[q][w] = xbuf[(w * 4 + q) * 64 + c.lane];
     // the slots of tile t+3, then the loads of tile t+2 into tile t's raw buffer (zero rows
     // past the split) once its slots, older than the 9 loads of tile t+1 and the slot load
     // just issued, have landed
@@ -1234,10 +1242,10 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
     f32x16 sc;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float4 x = xbuf[q * 64 + c.lane];
+      float4 x = xs[q][0];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) {
-        const float4 y = xbuf[(w * 4 + q) * 64 + c.lane];
+        const float4 y = xs[q][w];
         x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
       }
       sc[4 * q] = x.x; sc[4 * q + 1] = x.y; sc[4 * q + 2] = x.z; sc[4 * q + 3] = x.w;

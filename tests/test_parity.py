@@ -216,3 +216,17 @@ def test_work_list_one_long_request_among_short_ones():
     ref = run_oracle(w, rows=rows)
     compare(w, run_gpu(w, kernel="mfma"), ref, rows=rows)
     compare(w, run_gpu(w, kernel="mfma", num_splits=7), ref, rows=rows)
+
+
+def test_row_tile_boundaries():
+    """Requests whose row counts straddle the two item shapes: 1..32 rows (all four
+    wavefronts share the rows), 33..128 (one 32-row group per wavefront, some idle), and more
+    than 128 (several row tiles, the last one possibly of at most 32 rows)."""
+    rng = np.random.default_rng(18)
+    t = np.array([1, 31, 32, 33, 64, 96, 127, 128, 129, 160])
+    p = rng.integers(0, 700, len(t))
+    w = wl.build_workload("tiles", rng, 1, p, t, int((p + t).sum()) * 2)
+    say(f"row tiles: H=1 T={t.tolist()}")
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel="mfma"), ref)
+    compare(w, run_gpu(w, kernel="mfma", num_splits=3), ref)
