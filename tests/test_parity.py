@@ -180,6 +180,17 @@ def test_tp8_batch_sampled(kernel):
     compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
 
 
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_small_trees_sampled(kernel):
+    """H=64, T_r in 1..4: requests of 64 rows (two 32-row groups sharing the work), 128, 192
+    (a full row tile plus 64 rows) and 256."""
+    w = wl.small_trees()
+    rows = sample_rows(w, 384, seed=6)
+    say(f"small_trees, {kernel}, {len(rows)} sampled rows, T={w.tree_lens.tolist()}")
+    ref = run_oracle(w, rows=rows)
+    compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
+
+
 # ----------------------------------------------------------------------------- the device work list
 def test_work_list_more_requests_than_a_wavefront():
     """70 requests of mixed length: the plan scans the request tables in chunks of 64, and the

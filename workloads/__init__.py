@@ -302,8 +302,17 @@ def tp8_batch(seed: int = 0) -> Workload:
     return build_workload("tp8_batch", rng, 8, p, t, 1_048_576)
 
 
+def small_trees(seed: int = 0) -> Workload:
+    """16 requests, H=64, P_r log-uniform in [1024, 32768], T_r uniform in {1, 2, 3, 4}, bf16:
+    small draft trees with all heads on one GPU (64 to 256 rows per request)."""
+    rng = np.random.default_rng(seed)
+    p = np.floor(np.exp(rng.uniform(math.log(1024), math.log(32768), 16))).astype(np.int64)
+    t = rng.integers(1, 5, 16).astype(np.int64)
+    return build_workload("small_trees", rng, 64, p, t, 1_048_576)
+
+
 CONFIGS = {"tiny": tiny, "short": short, "long": long, "segmented": segmented, "stress": stress,
-           "tp8": tp8, "tp8_batch": tp8_batch}
+           "tp8": tp8, "tp8_batch": tp8_batch, "small_trees": small_trees}
 
 
 def make(name: str, seed: int = 0) -> Workload:
