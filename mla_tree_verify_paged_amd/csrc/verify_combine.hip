@@ -63,8 +63,6 @@ __device__ __forceinline__ void fma8(float4 &lo, float4 &hi, float w, const floa
   hi.z = fmaf(w, x1.z, hi.z); hi.w = fmaf(w, x1.w, hi.w);
 }
 
-// kBatch: splits whose rows a wavefront has in flight. Fewer keep more workgroups resident
-// (4 when the step has many rows), more shorten a row with many splits (8 for few rows).
 // the 2 output dims [dim0, dim0 + 2) of `row`
 __device__ void store2(const RunArgs &a, int64_t row, int dim0, float x, float y) {
   if (a.out_bf16) {
@@ -146,12 +144,18 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   // the scalars of splits lane + 64*i, i < kScal (kSlices > 1: rows with many splits read all
   // of them in this one round trip; otherwise only the first 64 here)
   constexpr int kScal = kSlices > 1 ? 4 : 1;
+  // (and, when the argmax is wanted, the split argmax of the same splits, so that picking the
+  // row's argmax needs no further round trip)
+  const bool want_arg = a.out_argmax != nullptr;
+  const int32_t *parg = ws.part_arg + base;
   float lsv[kScal], mxv[kScal];
+  int32_t agv[kScal];
 #pragma unroll
   for (int i = 0; i < kScal; ++i) {
     const int sp = lane + 64 * i;
     lsv[i] = sp < S ? plse[int64_t(sp) * stride] : -INFINITY;
     mxv[i] = sp < S ? pmax[int64_t(sp) * stride] : -INFINITY;
+    agv[i] = sp < S && want_arg ? parg[int64_t(sp) * stride] : -1;
   }
 
   // the request that owns token t: the last r with qo_indptr[r] <= t
@@ -215,22 +219,25 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
       const int s = s0 + lane;
       // the scalars of split s: held since the first round trip, or read now
       float ls = -INFINITY, mx = -INFINITY;
+      int32_t ag = -1;
       if (s0 < 64 * kScal) {
 #pragma unroll
         for (int i = 0; i < kScal; ++i)
           if (s0 == 64 * i) {
             ls = lsv[i];
             mx = mxv[i];
+            ag = agv[i];
           }
       } else if (s < S) {
         ls = plse[int64_t(s) * stride];
         mx = pmax[int64_t(s) * stride];
+        if (want_arg) ag = parg[int64_t(s) * stride];
       }
       const float wgt = ls == -INFINITY ? 0.f : expf(ls - M);
       W += wave_sum(wgt);
       if (arg < 0) {  // wave-uniform: the lowest split holding the largest max score
         const uint64_t hit = __ballot(s < S && mx == best);
-        if (hit) arg = ws.part_arg[base + int64_t(s0 + __builtin_ctzll(hit)) * stride];
+        if (hit) arg = __shfl(ag, int(__builtin_ctzll(hit)), 64);
       }
       // this wavefront's splits of the 64: s0 + wave + 4j, in batches of kBatch
       for (int j0 = 0; j0 < 64 / kWaves; j0 += kBatch) {
@@ -289,7 +296,7 @@ hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st)
     hipLaunchKernelGGL((combine_kernel<16, 4>), dim3(unsigned(rows * 4)), dim3(kThreads), 0, st,
                        a, ws);
   } else {
-    hipLaunchKernelGGL((combine_kernel<4, 1>), dim3(unsigned(rows)), dim3(kThreads), 0, st, a,
+    hipLaunchKernelGGL((combine_kernel<2, 1>), dim3(unsigned(rows)), dim3(kThreads), 0, st, a,
                        ws);
   }
   return hipGetLastError();
