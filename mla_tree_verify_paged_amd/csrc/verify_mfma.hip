@@ -188,13 +188,9 @@ __device__ __forceinline__ void dma_lanes(const void *src, uint32_t lds) {
 __device__ __forceinline__ void wait_tile_loads() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
-// The same, but leaving up to 9 loads in flight: the prologue issues the 9 loads of tile 1
-// after those of tile 0 (always; the slot fetch after them is skipped when no lane needs it),
-// and vector-memory loads complete in issue order, so tile 0 and q have landed.
-__device__ __forceinline__ void wait_loads_but_tile1() {
-  asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-}
-// The same, leaving 10 loads in flight (the narrow path's slot load plus a tile's 9).
+// The same, but leaving up to 10 loads in flight (a tile's 9 and a slot fetch issued after
+// them): vector-memory loads complete in issue order, so everything issued before those 10
+// has landed.
 __device__ __forceinline__ void wait_loads_but_10() {
   asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
 }
@@ -223,13 +219,15 @@ struct Ctx {
   int lane, half, col;
 };
 
-// Lane l fetches the slot of row (l & 7) of its wave's 8 rows of tile t (-1 past the split,
-// without a load). Consumed a tile later, after the wait for the tile loads.
+// Lane l fetches the slot of row (l & 7) of its wave's 8 rows of tile t. Consumed a tile
+// later, after the wait for the tile loads; plan_tile discards it for keys past the split.
+// Those keys read the split's last entry instead (k0 < k1 for every item), so that the load
+// is neither under a branch nor followed by a select on its value: either made the compiler
+// wait for it (and so for every load before it) right away.
 __device__ __forceinline__ int64_t fetch_slot(const Ctx &c, int t) {
-  int64_t v = -1;
   const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane & 7);
-  if (j < c.k1) v = (c.tree && j >= c.P) ? c.tree[j - c.P] : c.kvi[j];
-  return v;
+  const int jc = min(j, c.k1 - 1);
+  return (c.tree && jc >= c.P) ? c.tree[jc - c.P] : c.kvi[jc];
 }
 
 // The loads of one tile, prepared from the fetched slots: the row address each lane holds
@@ -586,17 +584,20 @@ __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits,
   st.mx = fmaxf(st.mx, tmax2);
   tmax = tmax2;
 
-  // lazy rescale of the running max (rare after the first tile)
+  // lazy rescale of the running max (rare after the first tile). A row whose running max is
+  // still -inf has O = 0 and lsum = 0 (every P it has seen was exp2(-inf) = 0), so it only
+  // takes the new max: the first tile of a split rescales nothing.
   const bool need = tmax > st.m + kRescale;
-  if (__any(need)) {
-    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - tmax) : 1.f;
-    if (need) st.m = tmax;
+  const bool rescale = need && st.m != -INFINITY;
+  if (__any(rescale)) {
+    const float alpha = rescale ? __builtin_amdgcn_exp2f(st.m - tmax) : 1.f;
     st.lsum *= alpha;
     matrix_drain();
 #pragma unroll
     for (int d = 0; d < kOBlocks; ++d) scale_acc(o[d], alpha);
     matrix_drain();
   }
+  if (need) st.m = tmax;
 }
 
 // ---- the balanced work list
@@ -889,10 +890,15 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
     s0 = fetch_slot(c, 0);
     s1 = fetch_slot(c, 1);
   }
+  // (the slot loads go out first: loads complete in issue order, so the tile loads that need
+  // the slots would otherwise wait for the query rows too)
+  asm volatile("" ::: "memory");
   // query fragments (B operand): row `col`, dims 16*kc + 8*half .. +8; all requested now,
   // made opaque to the optimiser only after the tile loads are issued (below)
+  // (every wavefront loads them, an idle one its clamped rows: with the loads under a branch
+  // the compiler's wait for the slots below would also wait for them)
   u32x4 qv[kQFrags];
-  if (active) {
+  {
     const uint4 *qrow = reinterpret_cast<const uint4 *>(
         static_cast<const uint16_t *>(a.q) + grow * kDim);
 #pragma unroll
@@ -942,9 +948,9 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
 
   f16x8 pf[2];
   if (ntiles > 0) {
-    // q and tile 0 have landed once at most the 9 loads of tile 1 are outstanding; tile 1 is
-    // waited for before the barrier that ends step 0
-    wait_loads_but_tile1();
+    // q and tile 0 have landed once at most the 9 loads of tile 1 and the slot fetch of tile 2
+    // are outstanding; tile 1 is waited for before the barrier that ends step 0
+    wait_loads_but_10();
     __syncthreads();
     TileLoads none;
     none.addr = 0;
