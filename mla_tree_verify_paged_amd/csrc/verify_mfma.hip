@@ -844,6 +844,27 @@ __device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan 
 }
 
 // One work item: split it.k of row tile it.rt of one request.
+// The slots of this wavefront's 8 rows of tile t into g_slots[t & 1][wave]: lane l < 16
+// loads dword l & 1 of row l >> 1's slot (keys past the split load a valid entry of the split
+// instead, and read_slots discards it). One load instruction per call.
+__device__ __forceinline__ void load_slots_lds(const Ctx &c, int t) {
+  if (c.lane < 2 * kRowsPerWave) {
+    const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane >> 1);
+    const int jc = min(j, c.k1 - 1);
+    const int64_t *e = (c.tree && jc >= c.P) ? c.tree + (jc - c.P) : c.kvi + jc;
+    dma_dword_lanes(reinterpret_cast<const uint32_t *>(e) + (c.lane & 1),
+                    lds_addr(reinterpret_cast<const char *>(&g_slots[t & 1][c.wave][0])));
+  }
+}
+// Lane l's slot of row l & 7 of tile t from g_slots (-1 past the split), once loaded.
+__device__ __forceinline__ int64_t read_slots(const Ctx &c, int t) {
+  const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane & 7);
+  // (a plain LDS read: the wait before it is an assembly statement with a memory clobber, so
+  // the read is not moved above it)
+  const int64_t v = g_slots[t & 1][c.wave][c.lane & 7];
+  return j < c.k1 ? v : -1;
+}
+
 template <bool kArgmax>
 __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, const Item &it) {
   const Segment &seg = it.seg;
@@ -882,33 +903,64 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
   char *const v0 = g_lds + kVOff;
   char *const v1 = g_lds + kVOff + kVTile;
 
-  // ---- prologue: the slots of tiles 0 and 1 and the query rows are requested together; the
-  // tile loads follow as soon as the slots arrive (loads complete in order, so that wait
-  // does not wait for q); the slots of tile 2 are fetched last
-  int64_t s0 = -1, s1 = -1;
-  if (ntiles > 0) {
-    s0 = fetch_slot(c, 0);
-    s1 = fetch_slot(c, 1);
-  }
-  // (the slot loads go out first: loads complete in issue order, so the tile loads that need
-  // the slots would otherwise wait for the query rows too)
-  asm volatile("" ::: "memory");
-  // query fragments (B operand): row `col`, dims 16*kc + 8*half .. +8; all requested now,
-  // made opaque to the optimiser only after the tile loads are issued (below)
-  // (every wavefront loads them, an idle one its clamped rows: with the loads under a branch
-  // the compiler's wait for the slots below would also wait for them)
-  u32x4 qv[kQFrags];
-  {
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(
-        static_cast<const uint16_t *>(a.q) + grow * kDim);
+  // ---- prologue. The query rows are staged through LDS in two halves (dims [0, 288) and
+  // [288, 576)), in the region of the two fp16 tiles, while tiles 0 and 1 load into the raw
+  // buffers: wavefront w's half block sits at kVOff + w * 32 * kQHStride, row r at
+  // r * kQHStride (36 units of 16 bytes and a pad unit, so that the fragment reads fall in
+  // distinct banks), and load i fills bytes [1024 i, 1024 i + 1024) of it, consecutive rows of
+  // q. Every load here is an assembly LDS load whose completion the code counts itself (the
+  // slots of tiles 0 and 1 also travel through LDS): a register result would make the
+  // compiler wait for every load before it. Issue order and waits:
+  //   slots of tiles 0, 1 (2) | half A (19) -> wait: slots landed
+  //   tile 0 rows (9) | tile 1 rows (9) | slots of tile 2 (1) -> wait: half A landed
+  //   half B (19) into the same place -> wait: everything
+  constexpr int kQHUnits = kQFrags + 1;             // 37
+  constexpr int kQHStride = 16 * kQHUnits;          // 592
+  constexpr int kQHChunks = 32 * kQHUnits;          // 1184
+  constexpr int kQHLoads = (kQHChunks + 63) / 64;   // 19
+  static_assert(kVOff + kWaves * 32 * kQHStride <= kXOff + kXBytes, "query halves fit in LDS");
+  char *const qblk = g_lds + kVOff + c.wave * 32 * kQHStride;
+  // the wavefront's rows, clamped to the request's last row (an idle wavefront stages that
+  // row only)
+  const int64_t row_first = seg.q0 * H + row0 + c.wave * 32;
+  const int64_t row_last = seg.q0 * H + rows_req - 1;
+  const int64_t base_row = min(row_first, row_last);
+  const int nrows = int(min(int64_t(32), row_last - base_row + 1));
+  const uint64_t qbase =
+      uint64_t(reinterpret_cast<uintptr_t>(a.q)) + uint64_t(base_row) * (2 * kDim);
+  const uint32_t qlim = uint32_t(nrows * (2 * kDim) - 16);
+  // chunk ch = 64 i + lane of half h is unit p = ch % 37 of row r = ch / 37, q unit
+  // 36 h + p of that row: byte 16 (ch + 35 r) + 576 h past the first row (the pad unit reads
+  // the unit after the half, inside the clamped rows)
+  auto stage_half = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kc = 0; kc < kQFrags; ++kc)
-      qv[kc] = __builtin_bit_cast(u32x4, qrow[2 * kc + c.half]);
-  }
+    for (int i = 0; i < kQHLoads; ++i) {
+      const int ch = 64 * i + c.lane;
+      const uint32_t voff = min(uint32_t(16 * (ch + 35 * (ch / kQHUnits)) + 576 * h), qlim);
+      if (64 * (i + 1) <= kQHChunks || ch < kQHChunks)
+        dma_row(qbase, voff, lds_addr(qblk) + 1024 * i);
+    }
+  };
+  u32x4 qv[kQFrags];
+  auto read_half = [&](int h) __attribute__((always_inline)) {
+    const char *qr = qblk + c.col * kQHStride + 16 * c.half;
+#pragma unroll
+    for (int k = 0; k < kQFrags / 2; ++k)
+      qv[h * (kQFrags / 2) + k] = *reinterpret_cast<const u32x4 *>(qr + 32 * k);
+  };
+  // (nothing the plan loaded is still in flight; saying so keeps the compiler from inserting
+  // a wait for it below, which would also wait for these loads)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   int64_t slot_vec = -1;
   if (ntiles > 0) {
-    const TileLoads t0 = plan_tile(c, 0, s0);
-    const TileLoads t1 = plan_tile(c, 1, s1);
+    load_slots_lds(c, 0);
+    load_slots_lds(c, 1);
+  }
+  stage_half(0);
+  asm volatile("s_waitcnt vmcnt(19)" ::: "memory");  // the slots of tiles 0 and 1
+  if (ntiles > 0) {
+    const TileLoads t0 = plan_tile(c, 0, read_slots(c, 0));
+    const TileLoads t1 = plan_tile(c, 1, read_slots(c, 1));
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, t0, lds_addr(raw0), i);
     issue_rope(c, t0, lds_addr(raw0));
@@ -919,8 +971,15 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
     publish_ok(c, 1, t1.ok);
     slot_vec = fetch_slot(c, 2);
   }
-  // keep the query fragments resident: without this the compiler re-reads q inside the tile
-  // loop. (Placed after every load is issued: it makes the wave wait for q.)
+  asm volatile("s_waitcnt vmcnt(19)" ::: "memory");  // half A
+  read_half(0);
+  // (half B overwrites what was just read: the reads must be complete)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  stage_half(1);
+  wait_tile_loads();
+  read_half(1);
+  // keep the query fragments resident: without this the compiler re-reads them inside the
+  // tile loop
   bf16x8 qf[kQFrags];
 #pragma unroll
   for (int kc = 0; kc < kQFrags; ++kc) {
@@ -1051,27 +1110,6 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
 constexpr int kNarrowFrags = kQFrags / kWaves;    // 9 score fragments per wavefront
 constexpr int kNarrowBlocks = kDBlocks / kWaves;  // 4 output dim blocks per wavefront
 
-// The slots of this wavefront's 8 rows of tile t into g_slots[t & 1][wave]: lane l < 16
-// loads dword l & 1 of row l >> 1's slot (keys past the split load a valid entry of the split
-// instead, and read_slots discards it). One load instruction per call.
-__device__ __forceinline__ void load_slots_lds(const Ctx &c, int t) {
-  if (c.lane < 2 * kRowsPerWave) {
-    const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane >> 1);
-    const int jc = min(j, c.k1 - 1);
-    const int64_t *e = (c.tree && jc >= c.P) ? c.tree + (jc - c.P) : c.kvi + jc;
-    dma_dword_lanes(reinterpret_cast<const uint32_t *>(e) + (c.lane & 1),
-                    lds_addr(reinterpret_cast<const char *>(&g_slots[t & 1][c.wave][0])));
-  }
-}
-// Lane l's slot of row l & 7 of tile t from g_slots (-1 past the split), once loaded.
-__device__ __forceinline__ int64_t read_slots(const Ctx &c, int t) {
-  const int j = c.k0 + t * kTK + c.wave * kRowsPerWave + (c.lane & 7);
-  // (a plain LDS read: the wait before it is an assembly statement with a memory clobber, so
-  // the read is not moved above it)
-  const int64_t v = g_slots[t & 1][c.wave][c.lane & 7];
-  return j < c.k1 ? v : -1;
-}
-
 template <bool kArgmax>
 __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws,
                                            const Item &it) {
@@ -1110,8 +1148,8 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
   float4 *const xbuf = reinterpret_cast<float4 *>(g_lds + kXOff);
   const int kc0 = kNarrowFrags * c.wave;  // this wavefront's first score fragment
 
-  // ---- prologue (as in the 128-row path): slots of tiles 0 and 1, this wavefront's query
-  // fragments, the loads of tiles 0 and 1, the slots of tile 2
+  // ---- prologue: slots of tiles 0 and 1, this wavefront's 9 query fragments (straight into
+  // registers: 9 loads per lane), the loads of tiles 0 and 1, the slots of tile 2
   int64_t s0 = fetch_slot(c, 0);
   int64_t s1 = fetch_slot(c, 1);
   u32x4 qv[kNarrowFrags];
