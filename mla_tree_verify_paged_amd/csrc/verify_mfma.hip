@@ -603,8 +603,9 @@ __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits,
 // ---- the balanced work list
 //
 // Request r (a usable segment with T_r > 0) has rt_r = ceil(T_r H / 128) row tiles and
-// kt_r = ceil(L_r / 32) key tiles. Its keys are cut into n_r splits of ct_r key tiles (the
-// last one may be shorter), and a work item is one (split, row tile) pair. Items are
+// kt_r = ceil(L_r / 32) key tiles. Its keys are cut into n_r = ceil(kt_r / ct_r) splits of
+// at most ct_r key tiles, as even as the count allows (split_range), and a work item is one
+// (split, row tile) pair. Items are
 // numbered request by request, split-major with the row tile fastest, so consecutive items
 // (which the launch places on one XCD) read the same key rows. Every workgroup computes the
 // same plan from the index tables, with no host involvement:
@@ -649,6 +650,17 @@ __device__ __forceinline__ int split_count(const ReqWork &q, int c, int forced) 
   if (q.rt == 0) return 0;
   const int ct = split_tiles(q.kt, c, forced);
   return (q.kt + ct - 1) / ct;
+}
+// Keys [k0, k1) of split k of n over L keys: the kt = ceil(L / 32) key tiles are dealt so
+// that the first kt % n splits take one tile more than the others (every split has at least
+// one tile, as n <= kt). Uneven splits let the workgroups with fewer tiles write their
+// partials while the others still compute, instead of every workgroup writing at once.
+__device__ __forceinline__ void split_range(int L, int k, int n, int &k0, int &k1) {
+  const int kt = (L - 1) / kTK + 1;
+  const int q = kt / n, r = kt % n;
+  const int t0 = k * q + min(k, r);
+  k0 = t0 * kTK;
+  k1 = min(L, (t0 + q + (k < r ? 1 : 0)) * kTK);
 }
 
 __device__ __forceinline__ int64_t wave_sum64(int64_t v) {
@@ -760,7 +772,6 @@ struct Item {
   int rt;        // row tile
   int k;         // split
   int n;         // splits of the request
-  int ct;        // key tiles per split
   int64_t prow;  // the request's first partial row
 };
 
@@ -792,7 +803,6 @@ __device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan 
     it.rt = int(w % q.rt);
     it.k = int(w / q.rt);
     it.n = n;
-    it.ct = split_tiles(q.kt, p.c, p.forced);
     it.prow = 0;
     return true;
   }
@@ -815,8 +825,7 @@ __device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan 
         it.rt = int(local % q.rt);
         it.k = int(local / q.rt);
         it.n = n;
-        it.ct = split_tiles(q.kt, p.c, p.forced);
-        it.prow = prow + sp - prows;
+            it.prow = prow + sp - prows;
       }
       // lane l's values to every lane (and to scalar registers)
       it.seg.q0 = __shfl(it.seg.q0, l, 64);
@@ -833,7 +842,6 @@ __device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan 
       it.rt = uniform(__shfl(it.rt, l, 64));
       it.k = uniform(__shfl(it.k, l, 64));
       it.n = uniform(__shfl(it.n, l, 64));
-      it.ct = uniform(__shfl(it.ct, l, 64));
       it.prow = uniform(__shfl(it.prow, l, 64));
       return true;
     }
@@ -892,9 +900,8 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
   const int tok = rho_c / H;
   const int64_t grow = (seg.q0 + tok) * int64_t(H) + rho_c % H;
 
-  // this split's keys: whole tiles (k * ct < kt, so k0 < L)
-  c.k0 = it.k * it.ct * kTK;
-  c.k1 = int(min(int64_t(seg.L), int64_t(c.k0) + int64_t(it.ct) * kTK));
+  // this split's keys: whole tiles, at least one (k0 < L)
+  split_range(seg.L, it.k, it.n, c.k0, c.k1);
   const int ntiles = (c.k1 - c.k0 + kTK - 1) / kTK;
 
   const LaneOffs lo = lane_offsets(c);
@@ -1136,8 +1143,7 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
   const int tok = rho_c / H;
   const int64_t grow = (seg.q0 + tok) * int64_t(H) + rho_c % H;
 
-  c.k0 = it.k * it.ct * kTK;
-  c.k1 = int(min(int64_t(seg.L), int64_t(c.k0) + int64_t(it.ct) * kTK));
+  split_range(seg.L, it.k, it.n, c.k0, c.k1);
   const int ntiles = (c.k1 - c.k0 + kTK - 1) / kTK;
 
   const LaneOffs lo = lane_offsets(c);
