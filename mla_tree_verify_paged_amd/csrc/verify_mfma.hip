@@ -1081,6 +1081,10 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
   const float ltot = st.lsum + swap_halves(st.lsum);
   if (!row_ok) return;
   const int64_t prow = it.prow + int64_t(it.k) * rows_req + rho;
+  if (prow >= ws.part_rows) {  // cannot happen: the workspace is sized for every plan
+    atomicOr(ws.status, 2u);   // VA_DEV_SEGMENT
+    return;
+  }
   if (it.k == 0 && c.half == 0) {
     RowInfo ri;
     ri.base = it.prow + rho;
@@ -1341,6 +1345,10 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
   const float ltot = st.lsum + swap_halves(st.lsum);
   if (!row_ok) return;
   const int64_t prow = it.prow + int64_t(it.k) * rows_req + rho;
+  if (prow >= ws.part_rows) {  // cannot happen: the workspace is sized for every plan
+    atomicOr(ws.status, 2u);   // VA_DEV_SEGMENT
+    return;
+  }
   float4 *po = reinterpret_cast<float4 *>(ws.part_o + prow * kLatent);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
 #pragma unroll

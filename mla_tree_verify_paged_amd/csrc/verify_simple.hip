@@ -177,6 +177,10 @@ simple_partial_kernel(RunArgs a, Workspace ws) {
   const int64_t x = row - seg.q0 * a.H;
   const int64_t base = int64_t(S) * seg.q0 * a.H + x;
   const int64_t prow = base + int64_t(s) * R;
+  if (prow >= ws.part_rows) {  // cannot happen: the workspace is sized for S splits of every row
+    if (lane == 0) atomicOr(ws.status, 2u);  // VA_DEV_SEGMENT
+    return;
+  }
   if (s == 0 && lane == 0) {
     RowInfo ri;
     ri.base = base;
