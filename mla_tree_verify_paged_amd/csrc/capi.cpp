@@ -69,6 +69,10 @@ int32_t compute_units() {
   return n;
 }
 
+// Bytes per partial-output dim: the MFMA kernel writes int16 codes with a scale per 128 dims,
+// the fp32-input kernel fp32.
+int part_elem_bytes(int32_t kernel) { return kernel == VA_KERNEL_MFMA ? 2 : 4; }
+
 struct Derived {
   int32_t kernel, splits, rows_per_block, row_tiles, grid;
   int64_t part_rows;
@@ -130,25 +134,27 @@ va_status derive(const verify_attn_config *c, Derived *d) {
     d->part_rows = s == 0 ? int64_t(va::kMfmaRowsPerBlock) * d->grid + rows_cap
                           : int64_t(s) * rows_cap;
   }
-  size_t off[6];
-  d->bytes = va::workspace_layout(d->part_rows, rows_cap, off);
+  size_t off[7];
+  d->bytes = va::workspace_layout(d->part_rows, rows_cap, part_elem_bytes(k), off);
   d->kernel = k;
   d->splits = s;
   return VA_OK;
 }
 
 void bind_workspace(verify_attn_ctx *x) {
-  size_t off[6];
+  size_t off[7];
   const int64_t rows_cap = x->cfg.max_q_tokens * x->cfg.num_heads;
-  va::workspace_layout(x->part_rows, rows_cap, off);
+  va::workspace_layout(x->part_rows, rows_cap, part_elem_bytes(x->kernel), off);
   char *b = static_cast<char *>(x->ws_base);
   x->ws.status = reinterpret_cast<uint32_t *>(b + off[0]);
   x->ws.zero_row = reinterpret_cast<const uint16_t *>(b + off[0] + va::kZeroRowOffset);
-  x->ws.part_o = reinterpret_cast<float *>(b + off[1]);
-  x->ws.part_lse = reinterpret_cast<float *>(b + off[2]);
-  x->ws.part_max = reinterpret_cast<float *>(b + off[3]);
-  x->ws.part_arg = reinterpret_cast<int32_t *>(b + off[4]);
-  x->ws.row_info = reinterpret_cast<va::RowInfo *>(b + off[5]);
+  x->ws.part_o = b + off[1];
+  x->ws.part_scale = reinterpret_cast<float *>(b + off[2]);
+  x->ws.part_i16 = part_elem_bytes(x->kernel) == 2;
+  x->ws.part_lse = reinterpret_cast<float *>(b + off[3]);
+  x->ws.part_max = reinterpret_cast<float *>(b + off[4]);
+  x->ws.part_arg = reinterpret_cast<int32_t *>(b + off[5]);
+  x->ws.row_info = reinterpret_cast<va::RowInfo *>(b + off[6]);
   x->ws.part_rows = x->part_rows;
   x->ws.rows_cap = rows_cap;
   x->ws.splits = x->splits;

@@ -4,7 +4,11 @@
 // R = max_q_tokens * H output rows:
 //   status   uint32 [64]            sticky VA_DEV_* bits in word 0
 //   zero_row uint16 [576]           zeros; key rows that must not be read load from here
-//   part_o   float  [N][512]        per-split normalised output O_s
+//   part_o                          per-split normalised output O_s, in one of two formats:
+//            float  [N][512]          fp32 (the fp32-input kernel), or
+//            int16  [N][512]          16-bit signed-normalised codes (the bf16 MFMA kernel):
+//                                     O_s[d] = code[d] * part_scale[4 * p + d / 128]
+//   part_scale float [N][4]         the code scale of each 128-dim group (int16 format only)
 //   part_lse float  [N]             per-split log-sum-exp (natural log); -inf for an empty split
 //   part_max float  [N]             per-split max score (natural-log units)
 //   part_arg int32  [N]             per-split argmax key position (-1 when empty)
@@ -35,7 +39,9 @@ struct RowInfo {
 struct Workspace {
   uint32_t *status;
   const uint16_t *zero_row;
-  float *part_o;
+  void *part_o;        // float [N][512] or int16 [N][512] (part_i16)
+  float *part_scale;   // [N][4], int16 format only
+  int32_t part_i16;    // 1: partial outputs are int16 codes with a scale per 128 dims
   float *part_lse;
   float *part_max;
   int32_t *part_arg;
@@ -77,17 +83,21 @@ constexpr size_t kStatusBytes = 64 * sizeof(uint32_t);
 constexpr size_t kZeroRowOffset = kStatusBytes;
 constexpr size_t kHeaderBytes = kZeroRowOffset + kDim * sizeof(uint16_t);
 
-// Byte offsets of the workspace regions for S splits and R rows; returns the total size.
-// Byte offsets of the workspace regions for N partial rows and R output rows; returns the
-// total size.
-inline size_t workspace_layout(int64_t N, int64_t R, size_t off[6]) {
+// Groups of 128 output dims that share one code scale in the int16 partial format.
+constexpr int kScaleGroups = 4;
+constexpr int kScaleGroupDims = kLatent / kScaleGroups;
+
+// Byte offsets of the workspace regions for N partial rows and R output rows, with partial
+// outputs of `elem_bytes` (4: fp32, 2: int16 codes) per dim; returns the total size.
+inline size_t workspace_layout(int64_t N, int64_t R, int elem_bytes, size_t off[7]) {
   size_t o = 0;
   off[0] = o; o = align256(o + kHeaderBytes);
-  off[1] = o; o = align256(o + size_t(N) * kLatent * sizeof(float));
-  off[2] = o; o = align256(o + size_t(N) * sizeof(float));
+  off[1] = o; o = align256(o + size_t(N) * kLatent * size_t(elem_bytes));
+  off[2] = o; o = align256(o + size_t(N) * kScaleGroups * sizeof(float));
   off[3] = o; o = align256(o + size_t(N) * sizeof(float));
-  off[4] = o; o = align256(o + size_t(N) * sizeof(int32_t));
-  off[5] = o; o = align256(o + size_t(R) * sizeof(RowInfo));
+  off[4] = o; o = align256(o + size_t(N) * sizeof(float));
+  off[5] = o; o = align256(o + size_t(N) * sizeof(int32_t));
+  off[6] = o; o = align256(o + size_t(R) * sizeof(RowInfo));
   return o;
 }
 

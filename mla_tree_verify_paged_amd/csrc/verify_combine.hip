@@ -74,15 +74,37 @@ __device__ void store2(const RunArgs &a, int64_t row, int dim0, float x, float y
   }
 }
 
+// A lane's slice of one partial row as loaded: kV fp32 values, or kV int16 codes (two per
+// word) and the scale of their 128-dim group. Decoded only where it is used, so that loads
+// stay in flight until then.
+template <int kV, bool kI16> struct PartSlice;
+template <int kV> struct PartSlice<kV, false> {
+  float x[kV];
+  __device__ __forceinline__ float value(int e) const { return x[e]; }
+  __device__ __forceinline__ float scale(int) const { return 1.f; }
+};
+template <int kV> struct PartSlice<kV, true> {
+  uint32_t w[kV / 2];
+  float sc[2];  // the scales of the lane's first and second kV/2 dims
+  __device__ __forceinline__ float value(int e) const {
+    const uint32_t u = w[e / 2];
+    return float((e & 1) ? int32_t(u) >> 16 : int32_t(u << 16) >> 16);
+  }
+  __device__ __forceinline__ float scale(int e) const { return sc[e < kV / 2 ? 0 : 1]; }
+};
+
 // One workgroup per (row, dim slice). kSlices = 1: the whole 512-dim row, each lane owning 8
-// dims ([4l, 4l+4) and [256+4l, 256+4l+4)); kSlices = 4 (steps with few rows, whose rows have
-// many splits): a quarter of the row per workgroup, each lane owning 2 dims, so a row's
-// splits are read by four workgroups on four compute units. kBatch: splits whose slices a
-// wavefront has in flight (fewer keep more workgroups resident).
-template <int kBatch, int kSlices>
+// dims, [4l, 4l+4) and [256+4l, 256+4l+4), so that the output stores are contiguous across
+// the wavefront; kSlices = 4 (steps with few rows, whose rows have many splits): a
+// quarter of the row per workgroup, each lane owning 2 dims, so a row's splits are read by
+// four workgroups on four compute units. kBatch: splits whose slices a wavefront has in
+// flight (fewer keep more workgroups resident). kI16: the partials are int16 codes with a
+// scale per 128 dims (the MFMA kernel's format), else fp32.
+template <int kBatch, int kSlices, bool kI16>
 __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace ws) {
   constexpr int kV = 8 / kSlices;           // dims per lane
   constexpr int kSliceDims = kLatent / kSlices;
+  static_assert(kSliceDims % kScaleGroupDims == 0 || kSlices == 1, "a slice in one group");
   __shared__ float red[kWaves - 1][kV][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -92,6 +114,9 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   // the lane's dims: kV consecutive ones at dim_a (kSlices > 1), or 4 at dim_a and 4 at
   // dim_a + 256
   const int dim_a = kSlices == 1 ? 4 * lane : slice * kSliceDims + kV * lane;
+  // the scale groups of those dims (int16 partials)
+  const int group_a = dim_a / kScaleGroupDims;
+  const int group_b = kSlices == 1 ? (dim_a + 256) / kScaleGroupDims : group_a;
 
   // where this row's partials are (written by the partial kernel for every row of a valid
   // request; for other rows it is stale or arbitrary, so it is only used once checked to stay
@@ -108,19 +133,39 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   }
   const float *plse = ws.part_lse + base;
   const float *pmax = ws.part_max + base;
-  const float *po = ws.part_o + base * kLatent + dim_a;
   const int64_t ostride = stride * kLatent;
-  auto load = [&](int sp, float *x) __attribute__((always_inline)) {
-    const float *src = po + sp * ostride;
-    if constexpr (kSlices == 1) {
-      const float4 u = *reinterpret_cast<const float4 *>(src);
-      const float4 v = *reinterpret_cast<const float4 *>(src + 256);
-      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-      x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  using Slice = PartSlice<kV, kI16>;
+  auto load = [&](int sp, Slice &x) __attribute__((always_inline)) {
+    if constexpr (kI16) {
+      const int16_t *src =
+          static_cast<const int16_t *>(ws.part_o) + base * kLatent + dim_a + sp * ostride;
+      const float *sc = ws.part_scale + (base + sp * stride) * kScaleGroups;
+      if constexpr (kSlices == 1) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(src);
+        const uint2 v = *reinterpret_cast<const uint2 *>(src + 256);
+        x.w[0] = u.x; x.w[1] = u.y; x.w[2] = v.x; x.w[3] = v.y;
+        // the split's four scales (one address for the whole wavefront), then the lane's two
+        const float4 s4 = *reinterpret_cast<const float4 *>(sc);
+        x.sc[0] = group_a == 0 ? s4.x : s4.y;
+        x.sc[1] = group_b == 2 ? s4.z : s4.w;
+      } else {
+        static_assert(kV == 2, "two dims per lane");
+        x.w[0] = *reinterpret_cast<const uint32_t *>(src);
+        x.sc[0] = x.sc[1] = sc[group_a];
+      }
     } else {
-      static_assert(kV == 2, "two dims per lane");
-      const float2 u = *reinterpret_cast<const float2 *>(src);
-      x[0] = u.x; x[1] = u.y;
+      const float *src = static_cast<const float *>(ws.part_o) + base * kLatent + dim_a +
+                         sp * ostride;
+      if constexpr (kSlices == 1) {
+        const float4 u = *reinterpret_cast<const float4 *>(src);
+        const float4 v = *reinterpret_cast<const float4 *>(src + 256);
+        x.x[0] = u.x; x.x[1] = u.y; x.x[2] = u.z; x.x[3] = u.w;
+        x.x[4] = v.x; x.x[5] = v.y; x.x[6] = v.z; x.x[7] = v.w;
+      } else {
+        static_assert(kV == 2, "two dims per lane");
+        const float2 u = *reinterpret_cast<const float2 *>(src);
+        x.x[0] = u.x; x.x[1] = u.y;
+      }
     }
   };
   auto store = [&](const float *v) __attribute__((always_inline)) {
@@ -135,7 +180,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   // Requested before the row is validated, so that one memory round trip serves all of them:
   // this wavefront's first kBatch splits and the scalars of the first 64 (all inside the
   // workspace, as checked above).
-  float x[kBatch][kV];
+  Slice x[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) {
     const int sp = wave + kWaves * j;
@@ -240,6 +285,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
         if (hit) arg = __shfl(ag, int(__builtin_ctzll(hit)), 64);
       }
       // this wavefront's splits of the 64: s0 + wave + 4j, in batches of kBatch
+#pragma unroll 1
       for (int j0 = 0; j0 < 64 / kWaves; j0 += kBatch) {
         if (s0 + wave + kWaves * j0 >= S) break;
         if (s0 > 0 || j0 > 0) {
@@ -255,8 +301,10 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
           const float wk = __shfl(wgt, sl, 64);
           // a split with zero weight contributes nothing (its row may be unwritten)
           if (s0 + sl < S && wk != 0.f) {
+            const float f0 = wk * x[j].scale(0), f1 = wk * x[j].scale(kV - 1);
 #pragma unroll
-            for (int e = 0; e < kV; ++e) acc[e] = fmaf(wk, x[j][e], acc[e]);
+            for (int e = 0; e < kV; ++e)
+              acc[e] = fmaf(e < kV / 2 ? f0 : f1, x[j].value(e), acc[e]);
           }
         }
       }
@@ -293,11 +341,18 @@ hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st)
   if (rows < 512) {
     // few rows: a quarter of a row per workgroup
     if (rows * 4 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((combine_kernel<16, 4>), dim3(unsigned(rows * 4)), dim3(kThreads), 0, st,
+    if (ws.part_i16)
+      hipLaunchKernelGGL((combine_kernel<16, 4, true>), dim3(unsigned(rows * 4)), dim3(kThreads),
+                         0, st, a, ws);
+    else
+      hipLaunchKernelGGL((combine_kernel<16, 4, false>), dim3(unsigned(rows * 4)),
+                         dim3(kThreads), 0, st, a, ws);
+  } else if (ws.part_i16) {
+    hipLaunchKernelGGL((combine_kernel<2, 1, true>), dim3(unsigned(rows)), dim3(kThreads), 0, st,
                        a, ws);
   } else {
-    hipLaunchKernelGGL((combine_kernel<2, 1>), dim3(unsigned(rows)), dim3(kThreads), 0, st, a,
-                       ws);
+    hipLaunchKernelGGL((combine_kernel<2, 1, false>), dim3(unsigned(rows)), dim3(kThreads), 0,
+                       st, a, ws);
   }
   return hipGetLastError();
 }

@@ -155,6 +155,28 @@ __device__ __forceinline__ void matrix_drain() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// Two values in [-1, 1] as packed 16-bit signed-normalised codes (v_cvt_pknorm_i16_f32:
+// clamped, scaled by 32767 and rounded), x in the low half.
+__device__ __forceinline__ uint32_t snorm16x2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(x, y));
+}
+
+// Stores the int16 codes of output block d (32 dims) of this lane's row, given as two codes per
+// word: c[gq][i] holds dims 32d + 8gq + 4half + 2i, +1. Lane pairs (l, l ^ 32) hold the same
+// row; two swaps per pair of groups give each lane 8 consecutive dims, so the block goes out
+// in two 16-byte stores per lane instead of four 8-byte ones.
+__device__ __forceinline__ void store_codes(int16_t *row_codes, int d, int half,
+                                            const uint32_t (&c)[4][2]) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    // lanes 0-31 end with dims 32d + 16k + 0..7, lanes 32-63 with 32d + 16k + 8..15
+    const auto s0 = __builtin_amdgcn_permlane32_swap(c[2 * k][0], c[2 * k + 1][0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(c[2 * k][1], c[2 * k + 1][1], false, false);
+    *reinterpret_cast<uint4 *>(row_codes + 32 * d + 16 * k + 8 * half) =
+        make_uint4(s0[0], s1[0], s0[1], s1[1]);
+  }
+}
+
 // One global_load_lds_dwordx4 from a scalar base: lane l's 16 bytes at base + voff land at
 // lds + 16*l. Inline assembly so that the compiler does not track the LDS write (it would
 // otherwise wait for these loads before every LDS read); the kernel waits for them itself
@@ -1092,16 +1114,37 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
     ri.stride = rows_req;
     ws.row_info[grow] = ri;
   }
-  float4 *po = reinterpret_cast<float4 *>(ws.part_o + prow * kLatent);
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  // int16 codes: each 128-dim group g (output blocks 4g .. 4g+3) is coded against its
+  // largest magnitude, am[g], and stored with the scale am[g] / (32767 l). The magnitudes
+  // are compared as integers (the bit patterns of non-negative floats order like the values).
+  uint32_t am[kScaleGroups];
 #pragma unroll
-  for (int d = 0; d < kDBlocks; ++d)
+  for (int g = 0; g < kScaleGroups; ++g) {
+    uint32_t m = 0;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq)
-      po[(32 * d + 8 * gq + 4 * c.half) / 4] =
-          make_float4(o[d][4 * gq] * inv, o[d][4 * gq + 1] * inv, o[d][4 * gq + 2] * inv,
-                      o[d][4 * gq + 3] * inv);
+    for (int d = 4 * g; d < 4 * g + 4; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = max(m, __float_as_uint(o[d][e]) & 0x7fffffffu);
+    am[g] = max(m, uint32_t(other_half(int(m))));
+  }
+  int16_t *pq = static_cast<int16_t *>(ws.part_o) + prow * kLatent;
+#pragma unroll
+  for (int d = 0; d < kDBlocks; ++d) {
+    const float a_g = __uint_as_float(am[d / 4]);
+    const float f = a_g > 0.f ? 1.f / a_g : 0.f;
+    uint32_t cw[4][2];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      cw[gq][0] = snorm16x2(o[d][4 * gq] * f, o[d][4 * gq + 1] * f);
+      cw[gq][1] = snorm16x2(o[d][4 * gq + 2] * f, o[d][4 * gq + 3] * f);
+    }
+    store_codes(pq, d, c.half, cw);
+  }
   if (c.half == 0) {
+    const float sl = ltot > 0.f ? 1.f / (32767.f * ltot) : 0.f;
+    *reinterpret_cast<float4 *>(ws.part_scale + kScaleGroups * prow) =
+        make_float4(__uint_as_float(am[0]) * sl, __uint_as_float(am[1]) * sl,
+                    __uint_as_float(am[2]) * sl, __uint_as_float(am[3]) * sl);
     const bool any = ltot > 0.f;
     ws.part_lse[prow] = any ? (st.m + log2f(ltot)) * kLn2 : -INFINITY;
     ws.part_max[prow] = any ? st.mx * kLn2 : -INFINITY;
@@ -1349,17 +1392,29 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
     atomicOr(ws.status, 2u);   // VA_DEV_SEGMENT
     return;
   }
-  float4 *po = reinterpret_cast<float4 *>(ws.part_o + prow * kLatent);
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  // int16 codes: this wavefront's 128 dims are one scale group (see the 128-row path)
+  static_assert(kNarrowBlocks * 32 == kScaleGroupDims, "a wavefront's dims are one group");
+  uint32_t amb = 0;
+#pragma unroll
+  for (int db = 0; db < kNarrowBlocks; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amb = max(amb, __float_as_uint(o[db][e]) & 0x7fffffffu);
+  const float am = __uint_as_float(max(amb, uint32_t(__shfl_xor(int(amb), 32, 64))));
+  const float f = am > 0.f ? 1.f / am : 0.f;
+  int16_t *pq = static_cast<int16_t *>(ws.part_o) + prow * kLatent;
 #pragma unroll
   for (int db = 0; db < kNarrowBlocks; ++db) {
     const int d = kNarrowBlocks * c.wave + db;
+    uint32_t cw[4][2];
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq)
-      po[(32 * d + 8 * gq + 4 * c.half) / 4] =
-          make_float4(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv, o[db][4 * gq + 2] * inv,
-                      o[db][4 * gq + 3] * inv);
+    for (int gq = 0; gq < 4; ++gq) {
+      cw[gq][0] = snorm16x2(o[db][4 * gq] * f, o[db][4 * gq + 1] * f);
+      cw[gq][1] = snorm16x2(o[db][4 * gq + 2] * f, o[db][4 * gq + 3] * f);
+    }
+    store_codes(pq, d, c.half, cw);
   }
+  if (c.half == 0)
+    ws.part_scale[kScaleGroups * prow + c.wave] = ltot > 0.f ? am / (32767.f * ltot) : 0.f;
   if (c.wave == 0 && c.half == 0) {
     if (it.k == 0) {
       RowInfo ri;

@@ -188,7 +188,7 @@ simple_partial_kernel(RunArgs a, Workspace ws) {
     ri.stride = int32_t(R);
     ws.row_info[row] = ri;
   }
-  float *po = ws.part_o + prow * kLatent;
+  float *po = static_cast<float *>(ws.part_o) + prow * kLatent;
   if (l > 0.f) {
     const float inv = 1.f / l;
 #pragma unroll

@@ -70,18 +70,20 @@ def test_workspace_bytes_positive_and_monotone_in_splits():
     a = B.verify_attn_workspace_bytes(cfg(num_splits=4))
     b = B.verify_attn_workspace_bytes(cfg(num_splits=8))
     assert 0 < a < b
-    # S * R * (512 + 3) * 4 bytes of partials, R = 16 * 64 rows
-    assert b >= 8 * 1024 * 515 * 4
+    # S * R partial rows of 512 int16 codes, 4 scales and 3 scalars, R = 16 * 64 rows
+    assert b >= 8 * 1024 * (512 * 2 + 7 * 4)
 
 
 def _align256(x):
     return (x + 255) // 256 * 256
 
 
-def _layout_bytes(part_rows, rows):
-    """The workspace layout the header documents: header, part_o, lse, max, arg, row_info."""
+def _layout_bytes(part_rows, rows, elem_bytes):
+    """The workspace layout the header documents: header, part_o (elem_bytes per dim),
+    part_scale (4 floats per partial row), lse, max, arg, row_info."""
     o = _align256(256 + 1152)
-    o = _align256(o + part_rows * 512 * 4)
+    o = _align256(o + part_rows * 512 * elem_bytes)
+    o = _align256(o + part_rows * 4 * 4)
     for _ in range(3):
         o = _align256(o + part_rows * 4)
     return _align256(o + rows * 16)
@@ -92,12 +94,12 @@ def test_workspace_size_follows_the_documented_layout():
     # MFMA kernel, splits chosen on the device: 128 rows per item, one item per compute unit
     # (256 when no device answers, as in this container), plus one row per output row
     auto = B.verify_attn_workspace_bytes(cfg(kernel=B.VA_KERNEL_MFMA))
-    assert auto == _layout_bytes(128 * 256 + rows, rows)
+    assert auto == _layout_bytes(128 * 256 + rows, rows, 2)
     # a fixed split count: that many partial rows per output row
     assert B.verify_attn_workspace_bytes(cfg(kernel=B.VA_KERNEL_MFMA, num_splits=5)) == \
-        _layout_bytes(5 * rows, rows)
+        _layout_bytes(5 * rows, rows, 2)
     assert B.verify_attn_workspace_bytes(cfg(kernel=B.VA_KERNEL_SIMPLE, num_splits=3)) == \
-        _layout_bytes(3 * rows, rows)
+        _layout_bytes(3 * rows, rows, 4)
 
 
 @pytest.mark.parametrize("bad", [
