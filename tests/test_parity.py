@@ -241,3 +241,51 @@ def test_row_tile_boundaries():
     ref = run_oracle(w)
     compare(w, run_gpu(w, kernel="mfma"), ref)
     compare(w, run_gpu(w, kernel="mfma", num_splits=3), ref)
+
+
+# ----------------------------------------------------------------------------- value ranges
+# Latent dims in four 128-dim groups at very different magnitudes: keys scaled by 2^6, 1,
+# 2^-6, 2^-12 per group and queries by the inverse powers of two, so every product q_d k_d, and
+# hence every score, is exactly that of the unscaled draw, while the values (the latent dims of
+# the keys) span 18 binary orders. The absolute 1e-2 bar cannot see an error in the small
+# groups, so each group is held to a bound relative to its own largest reference value:
+# 2^-8 covers the fp16 rounding of P (2^-11 of each weight) and of V, and the 16-bit partial
+# codes (one step = 2^-15 of the group's largest partial value) with room to spare; the
+# smallest group also absorbs fp16 subnormal rounding of V (at most 2^-25 absolute).
+GROUP_EXP = (6, 0, -6, -12)
+
+
+def _group_scaled(w):
+    import dataclasses
+    k = w.kv_rows_f32().copy()
+    q = w.q_f32().copy()
+    for g, e in enumerate(GROUP_EXP):
+        k[:, 128 * g:128 * (g + 1)] *= np.float32(2.0 ** e)
+        q[:, :, 128 * g:128 * (g + 1)] *= np.float32(2.0 ** -e)
+    return dataclasses.replace(w, name=w.name + "_groups", kv_rows=wl.to_bf16_bits(k),
+                               q=wl.to_bf16_bits(q))
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+@pytest.mark.parametrize("shape", ["rows1344", "rows24"])
+def test_value_groups_at_different_scales(kernel, shape):
+    rng = np.random.default_rng(77)
+    if shape == "rows1344":   # the 128-row path and the whole-row combine
+        base = wl.build_workload("groups", rng, 64, [3000, 700], [16, 5], 16384)
+    else:                     # the few-rows path and the quarter-row combine
+        base = wl.build_workload("groups", rng, 8, [5000], [3], 16384)
+    w = _group_scaled(base)
+    say(f"value groups {GROUP_EXP}, {shape}, {kernel}")
+    ref_o, ref_l, _ = run_oracle(w)
+    o, l, _, status = run_gpu(w, kernel=kernel)
+    assert status == 0
+    assert np.all(np.isfinite(o))
+    for g, e in enumerate(GROUP_EXP):
+        sl = slice(128 * g, 128 * (g + 1))
+        ref_max = float(np.max(np.abs(ref_o[:, sl])))
+        err = float(np.max(np.abs(o[:, sl] - ref_o[:, sl])))
+        say(f"  group {g} (x2^{e}): max|ref| {ref_max:.3e}, max err {err:.3e}")
+        assert err <= 2.0 ** -8 * ref_max + 2.0 ** -24, (g, err, ref_max)
+    # the scores did not change, so the lse matches the oracle's as in every other test
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(l), fin)
