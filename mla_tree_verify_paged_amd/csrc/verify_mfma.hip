@@ -1115,36 +1115,41 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
     ws.row_info[grow] = ri;
   }
   // int16 codes: each 128-dim group g (output blocks 4g .. 4g+3) is coded against its
-  // largest magnitude, am[g], and stored with the scale am[g] / (32767 l). The magnitudes
-  // are compared as integers (the bit patterns of non-negative floats order like the values).
-  uint32_t am[kScaleGroups];
+  // largest magnitude, am, and stored with the scale am / (32767 l). A group's 64
+  // accumulators per lane are read out of the matrix registers once and kept in VGPRs (the
+  // query fragments are dead by now) for both the maximum and the coding.
+  int16_t *pq = static_cast<int16_t *>(ws.part_o) + prow * kLatent;
+  float scl[kScaleGroups];
 #pragma unroll
   for (int g = 0; g < kScaleGroups; ++g) {
-    uint32_t m = 0;
+    float v[4][16];
 #pragma unroll
-    for (int d = 4 * g; d < 4 * g + 4; ++d)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) m = max(m, __float_as_uint(o[d][e]) & 0x7fffffffu);
-    am[g] = max(m, uint32_t(other_half(int(m))));
-  }
-  int16_t *pq = static_cast<int16_t *>(ws.part_o) + prow * kLatent;
+      for (int e = 0; e < 16; ++e) v[i][e] = o[4 * g + i][e];
+    float m = 0.f;
 #pragma unroll
-  for (int d = 0; d < kDBlocks; ++d) {
-    const float a_g = __uint_as_float(am[d / 4]);
-    const float f = a_g > 0.f ? 1.f / a_g : 0.f;
-    uint32_t cw[4][2];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      cw[gq][0] = snorm16x2(o[d][4 * gq] * f, o[d][4 * gq + 1] * f);
-      cw[gq][1] = snorm16x2(o[d][4 * gq + 2] * f, o[d][4 * gq + 3] * f);
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[i][e]));
+    m = fmaxf(m, other_half(m));
+    const float f = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t cw[4][2];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        cw[gq][0] = snorm16x2(v[i][4 * gq] * f, v[i][4 * gq + 1] * f);
+        cw[gq][1] = snorm16x2(v[i][4 * gq + 2] * f, v[i][4 * gq + 3] * f);
+      }
+      store_codes(pq, 4 * g + i, c.half, cw);
     }
-    store_codes(pq, d, c.half, cw);
+    scl[g] = m;
   }
   if (c.half == 0) {
     const float sl = ltot > 0.f ? 1.f / (32767.f * ltot) : 0.f;
     *reinterpret_cast<float4 *>(ws.part_scale + kScaleGroups * prow) =
-        make_float4(__uint_as_float(am[0]) * sl, __uint_as_float(am[1]) * sl,
-                    __uint_as_float(am[2]) * sl, __uint_as_float(am[3]) * sl);
+        make_float4(scl[0] * sl, scl[1] * sl, scl[2] * sl, scl[3] * sl);
     const bool any = ltot > 0.f;
     ws.part_lse[prow] = any ? (st.m + log2f(ltot)) * kLn2 : -INFINITY;
     ws.part_max[prow] = any ? st.mx * kLn2 : -INFINITY;
@@ -1394,13 +1399,18 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
   }
   // int16 codes: this wavefront's 128 dims are one scale group (see the 128-row path)
   static_assert(kNarrowBlocks * 32 == kScaleGroupDims, "a wavefront's dims are one group");
-  uint32_t amb = 0;
+  float v[kNarrowBlocks][16];
 #pragma unroll
   for (int db = 0; db < kNarrowBlocks; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) amb = max(amb, __float_as_uint(o[db][e]) & 0x7fffffffu);
-  const float am = __uint_as_float(max(amb, uint32_t(__shfl_xor(int(amb), 32, 64))));
-  const float f = am > 0.f ? 1.f / am : 0.f;
+    for (int e = 0; e < 16; ++e) v[db][e] = o[db][e];
+  float am = 0.f;
+#pragma unroll
+  for (int db = 0; db < kNarrowBlocks; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(v[db][e]));
+  am = fmaxf(am, other_half(am));
+  const float f = am > 0.f ? __builtin_amdgcn_rcpf(am) : 0.f;
   int16_t *pq = static_cast<int16_t *>(ws.part_o) + prow * kLatent;
 #pragma unroll
   for (int db = 0; db < kNarrowBlocks; ++db) {
@@ -1408,8 +1418,8 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
     uint32_t cw[4][2];
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      cw[gq][0] = snorm16x2(o[db][4 * gq] * f, o[db][4 * gq + 1] * f);
-      cw[gq][1] = snorm16x2(o[db][4 * gq + 2] * f, o[db][4 * gq + 3] * f);
+      cw[gq][0] = snorm16x2(v[db][4 * gq] * f, v[db][4 * gq + 1] * f);
+      cw[gq][1] = snorm16x2(v[db][4 * gq + 2] * f, v[db][4 * gq + 3] * f);
     }
     store_codes(pq, d, c.half, cw);
   }
