@@ -40,6 +40,8 @@ def test_long_full(kernel):
     say(f"long, {kernel}")
     ref = run_oracle(w)
     compare(w, run_gpu(w, kernel=kernel), ref)
+    # the launch bench.py times: out and lse, no argmax (the kernels' other instantiation)
+    compare(w, run_gpu(w, kernel=kernel, want_argmax=False), ref)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
@@ -49,6 +51,7 @@ def test_segmented_sampled(kernel):
     say(f"segmented, {kernel}, {len(rows)} sampled rows")
     ref = run_oracle(w, rows=rows)
     compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
+    compare(w, run_gpu(w, kernel=kernel, want_argmax=False), ref, rows=rows)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
@@ -58,6 +61,7 @@ def test_stress_sampled(kernel):
     say(f"stress, {kernel}, {len(rows)} sampled rows")
     ref = run_oracle(w, rows=rows)
     compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
+    compare(w, run_gpu(w, kernel=kernel, want_argmax=False), ref, rows=rows)
 
 
 # ----------------------------------------------------------------------------- seeded fuzz
@@ -169,6 +173,7 @@ def test_tp8_full(kernel):
     say(f"tp8, {kernel}")
     ref = run_oracle(w)
     compare(w, run_gpu(w, kernel=kernel), ref)
+    compare(w, run_gpu(w, kernel=kernel, want_argmax=False), ref)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
@@ -178,17 +183,19 @@ def test_tp8_batch_sampled(kernel):
     say(f"tp8_batch, {kernel}, {len(rows)} sampled rows")
     ref = run_oracle(w, rows=rows)
     compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
+    compare(w, run_gpu(w, kernel=kernel, want_argmax=False), ref, rows=rows)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
 def test_small_trees_sampled(kernel):
-    """H=64, T_r in 1..4: requests of 64 rows (two 32-row groups sharing the work), 128, 192
-    (a full row tile plus 64 rows) and 256."""
+    """H=64, T_r in 1..4: requests of 64 rows (a 128-row item with two of its four wavefronts
+    idle), 128, 192 (a full row tile plus 64 rows) and 256."""
     w = wl.small_trees()
     rows = sample_rows(w, 384, seed=6)
     say(f"small_trees, {kernel}, {len(rows)} sampled rows, T={w.tree_lens.tolist()}")
     ref = run_oracle(w, rows=rows)
     compare(w, run_gpu(w, kernel=kernel), ref, rows=rows)
+    compare(w, run_gpu(w, kernel=kernel, want_argmax=False), ref, rows=rows)
 
 
 # ----------------------------------------------------------------------------- the device work list
