@@ -131,8 +131,8 @@ typedef struct {
 /* Workspace bytes a config needs (0 if the config is invalid): per partial row about 1052
  * bytes for the MFMA kernel (512 16-bit codes, 4 group scales, 3 scalars) and about 2076 for
  * the fp32 kernel (512 floats, the same 7 words), with (128 * CUs + max_q_tokens * H) partial
- * rows for the MFMA kernel with num_splits = 0 (CUs = the current device's compute units, 256
- * when no device answers) and num_splits * max_q_tokens * H otherwise, plus 16 bytes per
+ * rows for the MFMA kernel with num_splits = 0 (CUs = the current device's compute units
+ * rounded up to a multiple of 8 and capped at 256; 256 when no device answers) and num_splits * max_q_tokens * H otherwise, plus 16 bytes per
  * output row. */
 size_t verify_attn_workspace_bytes(const verify_attn_config *cfg);
 

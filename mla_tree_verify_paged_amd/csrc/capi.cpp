@@ -9,6 +9,7 @@
 // allocated its workspace with a raw device malloc on first use, which broke graph capture
 // ("The Final Solder Joint", section "The Capture-Safety Constraint"); here the workspace is
 // bound once at create and run() only enqueues kernels.
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -127,10 +128,12 @@ va_status derive(const verify_attn_config *c, Derived *d) {
     d->row_tiles = int32_t(ceil_div(int64_t(c->max_q_per_req) * c->num_heads,
                                     va::kMfmaRowsPerBlock));
     // With s == 0 the work list is balanced on the device so that it holds at most `grid`
-    // items (one per compute unit, a multiple of 8) of kMfmaRowsPerBlock rows each when the
-    // requests have fewer row tiles than that (else one item per row tile), which bounds the
-    // partial rows by kMfmaRowsPerBlock * grid + rows_cap.
-    d->grid = int32_t(ceil_div(compute_units(), 8) * 8);
+    // items (one per compute unit, a multiple of 8, at most kMaxSplits so that no row has more
+    // splits than the combine takes) of kMfmaRowsPerBlock rows each when the requests have
+    // fewer row tiles than that (else one item per row tile), which bounds the partial rows by
+    // kMfmaRowsPerBlock * grid + rows_cap.
+    static_assert(va::kMaxSplits % 8 == 0, "the grid is a multiple of 8");
+    d->grid = int32_t(std::min<int64_t>(ceil_div(compute_units(), 8) * 8, va::kMaxSplits));
     d->part_rows = s == 0 ? int64_t(va::kMfmaRowsPerBlock) * d->grid + rows_cap
                           : int64_t(s) * rows_cap;
   }

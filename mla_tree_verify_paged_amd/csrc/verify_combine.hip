@@ -45,6 +45,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// The request that owns token t: the last r < bs with qo_indptr[r] <= t (0 when there is
+// none), from one lane-parallel read of the table per 64 requests rather than a binary search
+// of dependent reads. Wave-uniform. A table that is not nondecreasing gives some r, whose
+// segment the caller checks t against.
+__device__ __forceinline__ int owner_request(const RunArgs &a, int64_t t, int lane) {
+  int owner = 0;
+  for (int r0 = 0; r0 < a.bs; r0 += 64) {
+    const int r = r0 + lane;
+    const uint64_t le = __ballot(r < a.bs && a.qo_indptr[r] <= t);
+    if (le) owner = r0 + 63 - __builtin_clzll(le);
+    if (!(le >> 63)) break;  // the rest of a nondecreasing table lies past t
+  }
+  return owner;
+}
+
 // the 4 output dims [dim0, dim0 + 4) of `row`
 __device__ void store4(const RunArgs &a, int64_t row, int dim0, const float4 &v) {
   if (a.out_bf16) {
@@ -205,17 +220,12 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
     agv[i] = sp < S && want_arg ? parg[int64_t(sp) * stride] : -1;
   }
 
-  // the request that owns token t: the last r with qo_indptr[r] <= t
+  // the request that owns token t
   uint32_t bad = 0;
   bool ok = a.bs > 0 && row < a.num_tokens * a.H;
   if (ok) {
-    int lo = 0, hi = a.bs;  // answer in [lo, hi)
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.qo_indptr[mid] <= t) lo = mid; else hi = mid;
-    }
     Segment seg;
-    bad = load_segment(a, lo, seg);
+    bad = load_segment(a, owner_request(a, t, lane), seg);
     ok = bad == 0 && t >= seg.q0 && t < seg.q0 + seg.T;
     if (bad == 0 && !ok) bad = 8u;  // VA_DEV_TOKENS
     if (ok && !placed) {  // cannot happen: the partial kernel places every valid row
@@ -334,6 +344,144 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   }
 }
 
+// Steps with fewer than 512 rows, 16-bit partials: a quarter row per workgroup (lane l owns
+// dims 2l, 2l+1 of the slice's 128-dim scale group), and every split's codes requested in one
+// round trip. Such rows have many splits (tp8: 240), which the general kernel above reads 16
+// per wavefront per round trip. Wavefront w reads the codes of splits w + 4j (j < 64); lane s
+// holds the scalars of splits s, s + 64, s + 128, s + 192 and folds the slice's group scale
+// into the split's weight, so one cross-lane read per split gives the factor of its codes.
+// A row has at most kMaxSplits = 256 splits (the work list makes at most one item per compute
+// unit, capped at kMaxSplits, and a fixed split count is capped there too).
+__global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, Workspace ws) {
+  constexpr int kSlices = kScaleGroups;  // one scale group per workgroup
+  constexpr int kJ = kMaxSplits / kWaves;  // splits per wavefront
+  constexpr int kScal = kMaxSplits / 64;   // split scalars per lane
+  __shared__ float red[kWaves - 1][2][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x / kSlices;
+  const int slice = int(blockIdx.x % kSlices);
+  const int64_t t = row / a.H;
+  const int dim_a = slice * kScaleGroupDims + 2 * lane;
+
+  // where this row's partials are (checked to stay inside the workspace, as above)
+  const RowInfo ri = ws.row_info[row];
+  int S = ri.n;
+  int64_t base = ri.base, stride = ri.stride;
+  const bool placed = S >= 1 && S <= kMaxSplits && stride >= 1 && stride <= (1 << 28) &&
+                      base >= 0 && base + int64_t(S - 1) * stride < ws.part_rows;
+  if (!placed) {
+    S = 0;
+    base = 0;
+    stride = 0;
+  }
+  const int16_t *codes = static_cast<const int16_t *>(ws.part_o) + base * kLatent + dim_a;
+  const int64_t ostride = stride * kLatent;
+  const bool want_arg = a.out_argmax != nullptr;
+
+  // every load goes out before the row is validated
+  uint32_t cw[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int sp = wave + kWaves * j;
+    cw[j] = sp < S ? *reinterpret_cast<const uint32_t *>(codes + sp * ostride) : 0u;
+  }
+  float lsv[kScal], mxv[kScal], scv[kScal];
+  int32_t agv[kScal];
+#pragma unroll
+  for (int i = 0; i < kScal; ++i) {
+    const int sp = lane + 64 * i;
+    const bool in = sp < S;
+    const int64_t pr = base + int64_t(sp) * stride;
+    lsv[i] = in ? ws.part_lse[pr] : -INFINITY;
+    mxv[i] = in ? ws.part_max[pr] : -INFINITY;
+    agv[i] = in && want_arg ? ws.part_arg[pr] : -1;
+    scv[i] = in ? ws.part_scale[pr * kScaleGroups + slice] : 0.f;
+  }
+
+  // the request that owns token t
+  uint32_t bad = 0;
+  bool ok = a.bs > 0 && row < a.num_tokens * a.H;
+  if (ok) {
+    Segment seg;
+    bad = load_segment(a, owner_request(a, t, lane), seg);
+    ok = bad == 0 && t >= seg.q0 && t < seg.q0 + seg.T;
+    if (bad == 0 && !ok) bad = 8u;  // VA_DEV_TOKENS
+    if (ok && !placed) {  // cannot happen: the partial kernel places every valid row
+      ok = false;
+      bad = 2u;
+    }
+  } else {
+    bad = 8u;
+  }
+  if (!ok) {
+    if (threadIdx.x == 0 && slice == 0) {
+      atomicOr(ws.status, bad);
+      if (a.out_lse) a.out_lse[row] = -INFINITY;
+      if (a.out_argmax) a.out_argmax[row] = -1;
+    }
+    if (wave == 0) store2(a, row, dim_a, 0.f, 0.f);
+    return;
+  }
+
+  // the row's largest lse and max score (every wavefront computes the same)
+  float M = lsv[0], best = mxv[0];
+#pragma unroll
+  for (int i = 1; i < kScal; ++i) {
+    M = fmaxf(M, lsv[i]);
+    best = fmaxf(best, mxv[i]);
+  }
+  M = wave_max(M);
+  best = wave_max(best);
+  // the argmax: the lowest split holding the largest max score (split lane + 64 i)
+  int arg = -1;
+#pragma unroll
+  for (int i = kScal - 1; i >= 0; --i) {
+    const uint64_t hit = __ballot(mxv[i] == best);
+    if (hit) arg = __shfl(agv[i], int(__builtin_ctzll(hit)), 64);
+  }
+  float W = 0.f, acc0 = 0.f, acc1 = 0.f;
+  if (M != -INFINITY) {
+    // per split: its weight, and the weight times the group scale of its codes (zero for a
+    // split without visible keys, whose codes and scale may be unwritten)
+    float wsum = 0.f, f[kScal];
+#pragma unroll
+    for (int i = 0; i < kScal; ++i) {
+      const float w = lsv[i] == -INFINITY ? 0.f : expf(lsv[i] - M);
+      wsum += w;
+      f[i] = w != 0.f ? w * scv[i] : 0.f;
+    }
+    W = wave_sum(wsum);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      // split wave + 4j: its scalars are in lane (wave + 4j) % 64, slot 4j / 64
+      const float fk = __shfl(f[(kWaves * j) / 64], (wave + kWaves * j) & 63, 64);
+      if (fk != 0.f) {
+        acc0 = fmaf(fk, float(int32_t(cw[j] << 16) >> 16), acc0);
+        acc1 = fmaf(fk, float(int32_t(cw[j]) >> 16), acc1);
+      }
+    }
+  }
+  // the four wavefronts' sums meet in LDS; wavefront 0 finishes the slice
+  if (wave > 0) {
+    red[wave - 1][0][lane] = acc0;
+    red[wave - 1][1][lane] = acc1;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int k = 0; k < kWaves - 1; ++k) {
+    acc0 += red[k][0][lane];
+    acc1 += red[k][1][lane];
+  }
+  const float inv = M == -INFINITY ? 0.f : 1.f / W;
+  store2(a, row, dim_a, acc0 * inv, acc1 * inv);
+  if (lane == 0 && slice == 0) {
+    if (a.out_lse) a.out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
+    if (a.out_argmax) a.out_argmax[row] = arg;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st) {
@@ -344,8 +492,8 @@ hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st)
     // few rows: a quarter of a row per workgroup
     if (rows * 4 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (ws.part_i16)
-      hipLaunchKernelGGL((combine_kernel<16, 4, true>), dim3(unsigned(rows * 4)), dim3(kThreads),
-                         0, st, a, ws);
+      hipLaunchKernelGGL(combine_few_rows_kernel, dim3(unsigned(rows * 4)), dim3(kThreads), 0,
+                         st, a, ws);
     else
       hipLaunchKernelGGL((combine_kernel<16, 4, false>), dim3(unsigned(rows * 4)),
                          dim3(kThreads), 0, st, a, ws);
