@@ -358,6 +358,7 @@ template <> struct StepPlan<kFirst> {
   // conversion unit u: read after op rd(u), one pair converted after each of the next four
   // ops, written after op rd(u) + 4
   static constexpr int rd(int u) { return 2 + 4 * u; }
+  static constexpr int kCvLag = 0;
 };
 template <> struct StepPlan<kMain> {
   static constexpr int kOps = kQFrags + kNumPV;
@@ -372,7 +373,11 @@ template <> struct StepPlan<kMain> {
     }
     return t;
   }
+  // conversion unit u: read after op rd(u); its pairs are converted after ops rd(u) + 2 ..
+  // rd(u) + 5 (one matrix instruction more than the read needs to land) and it is written
+  // after op rd(u) + 5
   static constexpr int rd(int u) { return kPhaseA + 2 + 6 * u; }
+  static constexpr int kCvLag = 1;
   // the loads of tile t+2: one row after every second op from op 1 (rows 0..7 after ops
   // 1, 3, .., 15, the rope block after op 17), so that the four wavefronts' 36 loads reach
   // the address unit spread out rather than back to back; then the slots of tile t+3
@@ -389,6 +394,7 @@ template <> struct StepPlan<kLast> {
     return t;
   }
   static constexpr int rd(int u) { return -100; }
+  static constexpr int kCvLag = 0;
 };
 
 struct StepIO {
@@ -522,11 +528,12 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
       static_for<0, kRowsPerWave>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         constexpr int r0 = Plan::rd(u);
+        constexpr int c0 = r0 + Plan::kCvLag;  // the first pair converted after op c0 + 1
         if constexpr (p == r0)
           craw[u] = *reinterpret_cast<const u32x4 *>(cvr + kLatStride * u);
-        if constexpr (p > r0 && p <= r0 + 4) craw[u][p - r0 - 1] =
-            bf16pair_to_f16pair(craw[u][p - r0 - 1]);
-        if constexpr (p == r0 + 4) *reinterpret_cast<u32x4 *>(cvw + kVRow * u) = craw[u];
+        if constexpr (p > c0 && p <= c0 + 4) craw[u][p - c0 - 1] =
+            bf16pair_to_f16pair(craw[u][p - c0 - 1]);
+        if constexpr (p == c0 + 4) *reinterpret_cast<u32x4 *>(cvw + kVRow * u) = craw[u];
       });
     }
     // merge of the two score chains
