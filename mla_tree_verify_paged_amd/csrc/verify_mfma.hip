@@ -416,6 +416,25 @@ __device__ __forceinline__ void static_for(F &&f) {
 // P(t) = exp2(s*c2 - m) rounded to nearest-even fp16 (v_cvt_pk_f16_f32: unbiased, so the
 // denominator summed from the rounded values does not drift), in 8 parts of two keys; the
 // sum uses v_dot2.
+// Split in two halves so that a step can space the exponentials from their rounding:
+// p_exp computes the two exponentials of a part, p_round rounds, sums and places them.
+__device__ __forceinline__ f32x2 p_exp(int part, const f32x16 &s, float c2, float negm) {
+  const int ch = part >> 2, e = 2 * (part & 3);
+  f32x2 p;
+  p.x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ch + e], c2, negm));
+  p.y = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ch + e + 1], c2, negm));
+  return p;
+}
+__device__ __forceinline__ void p_round(int part, const f32x2 &p, float &lsum, f16x8 *pf) {
+  const int ch = part >> 2, e = 2 * (part & 3);
+  const f16x2v h = __builtin_convertvector(p, f16x2v);
+  const f16x2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+  lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, h), __builtin_bit_cast(fp16x2, ones),
+                                lsum, false);
+  pf[ch][e] = h.x;
+  pf[ch][e + 1] = h.y;
+}
+
 __device__ __forceinline__ void p_part(int part, const f32x16 &s, float c2, float negm,
                                        float &lsum, f16x8 *pf) {
   const int ch = part >> 2, e = 2 * (part & 3);
@@ -454,6 +473,7 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
   u32x4 fr[kDepth + 1];
   u32x4 craw[kRowsPerWave];
   f32x16 sa, sb;  // the two score chains
+  f32x2 pexp;     // the exponentials of the part of P(t) not yet rounded
   const float negm = neg_max(st);
 
   if constexpr (K == kLast && kCompute) {
@@ -513,8 +533,10 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
         sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kc], sa, 0, 0, 0);
       }
     }
-    // phase A: P(t), two keys after each of the first eight fragments
-    if constexpr (K == kMain && kCompute && p < 8) p_part(p, scur, c2, negm, st.lsum, pf);
+    // phase A: P(t), two keys after each of the first eight fragments; each part's
+    // exponentials are rounded and summed one fragment later
+    if constexpr (K == kMain && kCompute && p >= 1 && p <= 8) p_round(p - 1, pexp, st.lsum, pf);
+    if constexpr (K == kMain && kCompute && p < 8) pexp = p_exp(p, scur, c2, negm);
     // the loads of tile t+2 (zero rows past the split), then the slots of tile t+3
     if constexpr (K == kMain) {
       constexpr int dq = p - Plan::kDmaOp;
