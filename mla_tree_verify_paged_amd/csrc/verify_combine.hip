@@ -482,6 +482,150 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
   }
 }
 
+// Steps with more than 2048 rows, 16-bit partials: one wavefront per row, four rows per
+// workgroup, no LDS and no barrier. Such steps have few splits per row (segmented: about 3,
+// stress 4), so a row's reads take one round trip; a workgroup per row left three of its four
+// wavefronts with little or nothing to read, and every row's latency held a whole workgroup
+// slot. Lane l owns dims [4l, 4l+4) and
+// [256+4l, 256+4l+4) (groups l/32 and 2 + l/32), so the output stores are contiguous; it reads
+// the matching 8-byte code runs and the two group scales of each split, kB splits per round
+// trip, and lane s holds the scalars of splits s, s + 64, ...
+template <int kB>
+__global__ void __launch_bounds__(kThreads) combine_rows_kernel(RunArgs a, Workspace ws) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (row >= a.num_tokens * int64_t(a.H)) return;  // wave-uniform; nothing below synchronises
+  const int64_t t = row / a.H;
+  const int dim_a = 4 * lane;
+  const int ga = dim_a / kScaleGroupDims, gb = (dim_a + 256) / kScaleGroupDims;
+
+  const RowInfo ri = ws.row_info[row];
+  int S = ri.n;
+  int64_t base = ri.base, stride = ri.stride;
+  const bool placed = S >= 1 && S <= (1 << 20) && stride >= 1 && stride <= (1 << 28) &&
+                      base >= 0 && base + int64_t(S - 1) * stride < ws.part_rows;
+  if (!placed) {
+    S = 0;
+    base = 0;
+    stride = 0;
+  }
+  const int16_t *codes = static_cast<const int16_t *>(ws.part_o) + base * kLatent + dim_a;
+  const int64_t ostride = stride * kLatent;
+  const bool want_arg = a.out_argmax != nullptr;
+
+  // kB splits' code runs and group scales
+  uint2 ca[kB], cb[kB];
+  float sa[kB], sb[kB];
+  auto load = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int sp = s0 + j;
+      if (sp < S) {
+        const int16_t *src = codes + sp * ostride;
+        ca[j] = *reinterpret_cast<const uint2 *>(src);
+        cb[j] = *reinterpret_cast<const uint2 *>(src + 256);
+        const float *sc = ws.part_scale + (base + int64_t(sp) * stride) * kScaleGroups;
+        sa[j] = sc[ga];
+        sb[j] = sc[gb];
+      }
+    }
+  };
+  // the first kB splits and the scalars of the first 64 go out before the row is validated
+  load(0);
+  const int s_lane = lane;
+  const int64_t pr0 = base + int64_t(s_lane) * stride;
+  float ls0 = s_lane < S ? ws.part_lse[pr0] : -INFINITY;
+  float mx0 = s_lane < S ? ws.part_max[pr0] : -INFINITY;
+  int32_t ag0 = s_lane < S && want_arg ? ws.part_arg[pr0] : -1;
+
+  uint32_t bad = 0;
+  bool ok = a.bs > 0;
+  if (ok) {
+    Segment seg;
+    bad = load_segment(a, owner_request(a, t, lane), seg);
+    ok = bad == 0 && t >= seg.q0 && t < seg.q0 + seg.T;
+    if (bad == 0 && !ok) bad = 8u;  // VA_DEV_TOKENS
+    if (ok && !placed) {  // cannot happen: the partial kernel places every valid row
+      ok = false;
+      bad = 2u;
+    }
+  } else {
+    bad = 8u;
+  }
+  if (!ok) {
+    if (lane == 0) {
+      atomicOr(ws.status, bad);
+      if (a.out_lse) a.out_lse[row] = -INFINITY;
+      if (a.out_argmax) a.out_argmax[row] = -1;
+    }
+    store4(a, row, dim_a, make_float4(0.f, 0.f, 0.f, 0.f));
+    store4(a, row, dim_a + 256, make_float4(0.f, 0.f, 0.f, 0.f));
+    return;
+  }
+
+  // the row's largest lse and max score over all splits
+  float M = ls0, best = mx0;
+  for (int s0 = 64; s0 < S; s0 += 64) {
+    const int sp = s0 + lane;
+    if (sp < S) {
+      const int64_t pr = base + int64_t(sp) * stride;
+      M = fmaxf(M, ws.part_lse[pr]);
+      best = fmaxf(best, ws.part_max[pr]);
+    }
+  }
+  M = wave_max(M);
+  best = wave_max(best);
+
+  float W = 0.f;
+  int arg = -1;
+  float acc[8] = {};
+  if (M != -INFINITY) {
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int sp = s0 + lane;
+      float ls = ls0, mx = mx0;
+      int32_t ag = ag0;
+      if (s0 > 0) {
+        const int64_t pr = base + int64_t(sp) * stride;
+        ls = sp < S ? ws.part_lse[pr] : -INFINITY;
+        mx = sp < S ? ws.part_max[pr] : -INFINITY;
+        ag = sp < S && want_arg ? ws.part_arg[pr] : -1;
+      }
+      const float wgt = ls == -INFINITY ? 0.f : expf(ls - M);
+      W += wave_sum(wgt);
+      if (arg < 0) {  // the lowest split holding the largest max score
+        const uint64_t hit = __ballot(sp < S && mx == best);
+        if (hit) arg = __shfl(ag, int(__builtin_ctzll(hit)), 64);
+      }
+#pragma unroll 1
+      for (int j0 = 0; j0 < 64 && s0 + j0 < S; j0 += kB) {
+        if (s0 > 0 || j0 > 0) load(s0 + j0);
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+          const float wk = __shfl(wgt, j0 + j, 64);
+          // a split with zero weight contributes nothing (its codes may be unwritten)
+          if (s0 + j0 + j < S && wk != 0.f) {
+            const float fa = wk * sa[j], fb = wk * sb[j];
+            const uint32_t w4[4] = {ca[j].x, ca[j].y, cb[j].x, cb[j].y};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t u = w4[e / 2];
+              const float v = float((e & 1) ? int32_t(u) >> 16 : int32_t(u << 16) >> 16);
+              acc[e] = fmaf(e < 4 ? fa : fb, v, acc[e]);
+            }
+          }
+        }
+      }
+    }
+  }
+  const float inv = M == -INFINITY ? 0.f : 1.f / W;
+  store4(a, row, dim_a, make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv));
+  store4(a, row, dim_a + 256, make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv));
+  if (lane == 0) {
+    if (a.out_lse) a.out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
+    if (a.out_argmax) a.out_argmax[row] = arg;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st) {
@@ -497,6 +641,12 @@ hipError_t launch_combine(const RunArgs &a, const Workspace &ws, hipStream_t st)
     else
       hipLaunchKernelGGL((combine_kernel<16, 4, false>), dim3(unsigned(rows * 4)),
                          dim3(kThreads), 0, st, a, ws);
+  } else if (ws.part_i16 && rows > 2048) {
+    // many rows, few splits each: a wavefront per row (segmented 28.8 -> 17.7 us, stress
+    // 23.8 -> 15.0 us); with up to 2048 rows a row has more splits (long: 32), which the four
+    // wavefronts of a workgroup per row read faster (long 11.5 against 13.8 us)
+    hipLaunchKernelGGL(combine_rows_kernel<4>, dim3(unsigned((rows + kWaves - 1) / kWaves)),
+                       dim3(kThreads), 0, st, a, ws);
   } else if (ws.part_i16) {
     hipLaunchKernelGGL((combine_kernel<2, 1, true>), dim3(unsigned(rows)), dim3(kThreads), 0, st,
                        a, ws);

@@ -55,26 +55,31 @@ def test_prefix_shorter_than_tree_is_flagged(kernel):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_tokens_not_covered_by_qo_indptr(kernel):
-    """num_tokens = 7 but qo_indptr covers 5 tokens: rows of tokens 5 and 6 are empty."""
+@pytest.mark.parametrize("h,t", [(4, 5), (64, 16), (64, 40)])
+def test_tokens_not_covered_by_qo_indptr(kernel, h, t):
+    """num_tokens = T + 2 but qo_indptr covers T tokens: the rows of the last two tokens are
+    empty. H*(T+2) = 28, 1152 and 2688 rows: the three launch shapes of the combine."""
     import torch
     from mla_tree_verify_paged_amd import VerifyAttn
     from mla_tree_verify_paged_amd.device_inputs import to_device
-    w = wl.build_workload("tok", np.random.default_rng(23), 4, [16], [5], 64)
+    w = wl.build_workload("tok", np.random.default_rng(23), h, [300], [t], 512)
     dev = to_device(w)
+    n = t + 2
     q = torch.cat([dev["q"], dev["q"][:2]])
-    va = VerifyAttn(4, max_batch=1, max_q_per_req=5, max_q_tokens=7, kernel=kernel)
-    out = torch.full((7, 4, 512), float("nan"), device="cuda")
-    lse = torch.zeros((7, 4), device="cuda")
+    va = VerifyAttn(h, max_batch=1, max_q_per_req=t, max_q_tokens=n, kernel=kernel)
+    out = torch.full((n, h, 512), float("nan"), device="cuda")
+    lse = torch.zeros((n, h), device="cuda")
+    am = torch.full((n, h), 7, dtype=torch.int32, device="cuda")
     va.run(q, dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"], dev["qo_indptr"],
-           dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, None, bs=1, num_tokens=7)
+           dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, am, bs=1, num_tokens=n)
     st = va.read_device_status()
     assert st & B.VA_DEV_TOKENS
     o = out.cpu().numpy()
-    assert np.all(o[5:] == 0) and np.all(np.isfinite(o))
-    assert np.all(lse.cpu().numpy()[5:] == -np.inf)
+    assert np.all(o[t:] == 0) and np.all(np.isfinite(o))
+    assert np.all(lse.cpu().numpy()[t:] == -np.inf)
+    assert np.all(am.cpu().numpy()[t:] == -1)
     ref = run_oracle(w)
-    compare(w, (o[:5].reshape(-1, 512).astype(np.float64), lse.cpu().numpy()[:5].ravel(), None,
+    compare(w, (o[:t].reshape(-1, 512).astype(np.float64), lse.cpu().numpy()[:t].ravel(), None,
                 0), ref)
 
 
