@@ -8,16 +8,20 @@
 // and the argmax is the argmax of the split holding the largest max score (lowest split,
 // hence lowest key position, on ties).
 //
-// One workgroup per row (a quarter of a row when the step has fewer than 512 rows). Every
-// wavefront reads the per-split scalars lane-parallel (lane s holds split s) and derives the
-// same max, weights and argmax; the splits' partial rows are dealt to the four wavefronts
-// (split s to wavefront s % 4), each lane owning 8 output dims (2 in a quarter row), with 2
-// (16 in a quarter row) splits' slices in flight per wavefront; the four partial sums meet in
-// LDS. A row with many splits (few rows, long keys) is thus read by 256 threads or more. The
-// partials are fp32, or 16-bit signed-normalised codes with one scale per 128 dims (the MFMA
-// kernel's format, half the bytes). The combine also owns output validation: a row whose token belongs to no valid request is written empty (out 0,
-// lse -inf, argmax -1) and the matching status bit is set, so every output element is defined
-// whatever the device-side tables hold.
+// The partials are fp32 (the fp32-input kernel), or 16-bit signed-normalised codes with one
+// scale per 128 dims (the MFMA kernel's format, half the bytes). Three launch shapes, chosen by
+// the step's row count (rows with few rows have many splits, and the reverse):
+//  - combine_kernel: one workgroup per row (a quarter of a row below 512 rows, fp32 partials).
+//    Every wavefront reads the per-split scalars lane-parallel (lane s holds split s) and
+//    derives the same max, weights and argmax; the splits' partial rows are dealt to the four
+//    wavefronts (split s to wavefront s % 4), each lane owning 8 output dims (2 in a quarter
+//    row), and the four partial sums meet in LDS;
+//  - combine_few_rows_kernel (16-bit partials, below 512 rows): a quarter row per workgroup,
+//    every split's codes in one round trip;
+//  - combine_rows_kernel (16-bit partials, over 2048 rows): one wavefront per row.
+// The combine also owns output validation: a row whose token belongs to no valid request is
+// written empty (out 0, lse -inf, argmax -1) and the matching status bit is set, so every
+// output element is defined whatever the device-side tables hold.
 #include <math.h>
 
 #include "va_internal.h"
