@@ -42,6 +42,15 @@
  *   out_argmax[t,h] = the smallest visible key position j with the largest s_j.
  *   A row with no visible key gets out = 0, lse = -inf, argmax = -1.
  *
+ * Arithmetic: fp32 inputs run in fp32 throughout (the simple kernel). bf16 inputs run on
+ *   the matrix cores: scores from bf16 products accumulated in fp32; P rounded to fp16
+ *   (nearest even) and the value rows converted to fp16 (exact for |v| < 65504; larger
+ *   values saturate) for the P.V products, accumulated in fp32, with the denominator summed
+ *   from the rounded P; each key split's normalised partial stored as 16-bit codes with one
+ *   scale per 128 dims (one code step is 1/32767 of that group's largest value). The output
+ *   error is thus relative to the magnitude of the value rows: a small multiple of 2^-11 of
+ *   the largest visible value at worst, far less where the rounding errors average out.
+ *
  * Conventions
  *   Ownership: every tensor argument is caller-owned device memory. The library owns the
  *     context and, only when the config brings no workspace, a workspace it allocates in
@@ -132,12 +141,13 @@ typedef struct {
  * bytes for the MFMA kernel (512 16-bit codes, 4 group scales, 3 scalars) and about 2076 for
  * the fp32 kernel (512 floats, the same 7 words), with (128 * CUs + max_q_tokens * H) partial
  * rows for the MFMA kernel with num_splits = 0 (CUs = the current device's compute units
- * rounded up to a multiple of 8 and capped at 256; 256 when no device answers) and num_splits * max_q_tokens * H otherwise, plus 16 bytes per
- * output row. */
+ * rounded up to a multiple of 8 and capped at 256; 256 when no device answers) and
+ * num_splits * max_q_tokens * H otherwise, plus 16 bytes per output row. */
 size_t verify_attn_workspace_bytes(const verify_attn_config *cfg);
 
 /* Validates `cfg`, binds or allocates the workspace, clears its status words and a row of
- * zeros the kernels read in place of unusable key rows (synchronously, on the null stream). Returns VA_OK and sets *out, or an error and leaves *out NULL. */
+ * zeros the kernels read in place of unusable key rows (synchronously, on the null stream).
+ * Returns VA_OK and sets *out, or an error and leaves *out NULL. */
 va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **out);
 
 /*
