@@ -121,8 +121,18 @@ def test_request_without_tree_tokens(kernel):
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
-def test_bf16_output(kernel):
-    w = wl.short()
+@pytest.mark.parametrize("shape", ["short", "rows2560", "rows48"])
+def test_bf16_output(kernel, shape):
+    """bf16 output in each combine launch shape: 1024 rows (a workgroup per row), 2560 rows
+    (a wavefront per row) and 48 rows (a quarter row per workgroup)."""
+    if shape == "short":
+        w = wl.short()
+    elif shape == "rows2560":
+        w = wl.build_workload("bf16out", np.random.default_rng(15), 64, [900, 2500], [24, 16],
+                              8192)
+    else:
+        w = wl.build_workload("bf16out", np.random.default_rng(16), 8, [3000, 1200], [4, 2],
+                              8192)
     ref = run_oracle(w)
     o, l, a, st = run_gpu(w, kernel=kernel, out_dtype="bf16")
     err = np.abs(o - ref[0])
