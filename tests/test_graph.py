@@ -15,26 +15,29 @@ pytestmark = [pytest.mark.gpu,
 KERNELS = ["simple", "mfma"]
 
 
-def make(seed, p, t):
-    return wl.build_workload(f"g{seed}", np.random.default_rng(seed), 64, [p], [t], 65536)
+def make(seed, p, t, h=64):
+    return wl.build_workload(f"g{seed}", np.random.default_rng(seed), h, [p], [t], 65536)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_graph_replay_with_new_buffer_contents(kernel):
+@pytest.mark.parametrize("h,max_t", [(64, 16), (64, 40), (8, 4)])
+def test_graph_replay_with_new_buffer_contents(kernel, h, max_t):
+    """H*T = 1024, 2560 and 32 rows: the three launch shapes of the combine (and, at H=8, the
+    partial kernel's few-rows path)."""
     from mla_tree_verify_paged_amd import VerifyAttn
     from mla_tree_verify_paged_amd.device_inputs import to_device
-    max_t, max_l = 16, 4000
-    va = VerifyAttn(64, max_batch=1, max_q_per_req=max_t, max_q_tokens=max_t, kernel=kernel)
+    max_l = 4000
+    va = VerifyAttn(h, max_batch=1, max_q_per_req=max_t, max_q_tokens=max_t, kernel=kernel)
     # static buffers sized for the largest step
-    q = torch.zeros((max_t, 64, 576), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((max_t, h, 576), dtype=torch.bfloat16, device="cuda")
     pool = torch.zeros((65536, 576), dtype=torch.bfloat16, device="cuda")
     idx = torch.zeros(max_l, dtype=torch.int64, device="cuda")
     kv_indptr = torch.zeros(2, dtype=torch.int32, device="cuda")
     qo_indptr = torch.zeros(2, dtype=torch.int64, device="cuda")
     mask = torch.zeros(max_t * max_l, dtype=torch.uint8, device="cuda")
     mask_indptr = torch.zeros(2, dtype=torch.int64, device="cuda")
-    out = torch.zeros((max_t, 64, 512), dtype=torch.float32, device="cuda")
-    lse = torch.zeros((max_t, 64), dtype=torch.float32, device="cuda")
+    out = torch.zeros((max_t, h, 512), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((max_t, h), dtype=torch.float32, device="cuda")
 
     def load(w):
         d = to_device(w)
@@ -54,7 +57,7 @@ def test_graph_replay_with_new_buffer_contents(kernel):
 
     # the graph is recorded once with num_tokens = max_t; steps with fewer tokens leave the
     # extra rows empty (qo_indptr covers fewer tokens), which the C ABI reports in its status
-    w0 = make(100, 3000, 16)
+    w0 = make(100, 3000, max_t, h)
     load(w0)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -68,8 +71,9 @@ def test_graph_replay_with_new_buffer_contents(kernel):
         step()
     torch.cuda.synchronize()
 
-    for seed, p, t in ((101, 3000, 16), (102, 1200, 16), (103, 3984, 16), (104, 2500, 16)):
-        w = make(seed, p, t)
+    for seed, p in ((101, 3000), (102, 1200), (103, 4000 - max_t), (104, 2500)):
+        t = max_t
+        w = make(seed, p, t, h)
         load(w)
         g.replay()
         torch.cuda.synchronize()
