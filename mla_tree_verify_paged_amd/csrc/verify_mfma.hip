@@ -181,28 +181,27 @@ __device__ __forceinline__ void store_codes(int16_t *row_codes, int d, int half,
 // lds + 16*l. Inline assembly so that the compiler does not track the LDS write (it would
 // otherwise wait for these loads before every LDS read); the kernel waits for them itself
 // before the data is read, and a barrier orders them for the other wavefronts.
-// The scalar base comes from v_readlane just before: a vector-memory instruction that reads
-// an SGPR written by a VALU instruction needs 5 wait states on this generation, and the
-// compiler does not look inside the asm, so the asm supplies them (s_mov + s_nop 4 = 6; they
-// also cover the M0 write before the LDS DMA).
+// The LDS address travels in M0, which the asm takes as an input operand ("{m0}"), so the
+// compiler writes M0 itself and knows it is read here. Wait states the compiler cannot see
+// through the asm are supplied inside it: the scalar base comes from v_readlane just before,
+// and a vector-memory instruction that reads an SGPR written by a VALU instruction needs 5 wait
+// states on this generation (the LDS DMA also needs 1 after the M0 write): s_nop 4 gives 5.
 __device__ __forceinline__ void dma_row(uint64_t base, uint32_t voff, uint32_t lds) {
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
       "s_nop 4\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(voff), "s"(base), "s"(lds)
-      : "memory", "m0");
+      : "v"(voff), "s"(base), "{m0}"(lds)
+      : "memory");
 }
-// The same from a per-lane 64-bit address.
+// The same from a per-lane 64-bit address (1 wait state after the M0 write).
 __device__ __forceinline__ void dma_lanes(const void *src, uint32_t lds) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
-      : "v"(src), "s"(lds)
-      : "memory", "m0");
+      : "v"(src), "{m0}"(lds)
+      : "memory");
 }
 
 // Waits until this thread's outstanding vector-memory loads (the tile loads among them) are
@@ -220,12 +219,11 @@ __device__ __forceinline__ void wait_loads_but_10() {
 // lds + 4*l.
 __device__ __forceinline__ void dma_dword_lanes(const void *src, uint32_t lds) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dword %0, off"
       :
-      : "v"(src), "s"(lds)
-      : "memory", "m0");
+      : "v"(src), "{m0}"(lds)
+      : "memory");
 }
 
 // Per-workgroup constants of one split.
