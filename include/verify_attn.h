@@ -35,7 +35,8 @@
  *     tokens' slots from out_cache_loc, told apart by the kv_indptr offsets: "The Final
  *     Solder Joint", section "The Three-Edits Sequence".)
  *   key j is visible iff j < P_r or
- *   custom_mask[mask_indptr[r] + i*L_r + j] != 0 (prefix columns are never read);
+ *   custom_mask[mask_indptr[r] + i*L_r + j] != 0 (prefix columns are ignored: a kernel may
+ *   read them but never uses their value);
  *   s_j = sm_scale * <q[t,h,0:576], kv[slot_j,0:576]>,  t = qo_indptr[r] + i;
  *   out[t,h,0:512] = sum_j softmax(s)_j * kv[slot_j, 0:512] over the visible keys;
  *   out_lse[t,h] = natural-log sum-exp of the visible s_j;
@@ -44,19 +45,28 @@
  *
  * Arithmetic: fp32 inputs run in fp32 throughout (the simple kernel). bf16 inputs run on
  *   the matrix cores: scores from bf16 products accumulated in fp32; P rounded to fp16
- *   (nearest even) and the value rows converted to fp16 (exact for |v| < 65504; larger
- *   values saturate) for the P.V products, accumulated in fp32, with the denominator summed
- *   from the rounded P; each key split's normalised partial stored as 16-bit codes with one
- *   scale per 128 dims (one code step is 1/32767 of that group's largest value). The output
- *   error is thus relative to the magnitude of the value rows: a small multiple of 2^-11 of
- *   the largest visible value at worst, far less where the rounding errors average out.
+ *   (nearest even) and the value dims converted from bf16 to fp16 with round-toward-zero for
+ *   the P.V products, accumulated in fp32, with the denominator summed from the rounded P;
+ *   each key split's normalised partial stored as 16-bit codes with one scale per 128 dims
+ *   (one code step is 1/32767 of that group's largest value). The output error is thus
+ *   relative to the magnitude of the value rows: a small multiple of 2^-11 of the largest
+ *   visible value at worst, far less where the rounding errors average out.
+ *   Value range (bf16 inputs): the fp16 conversion is exact for 2^-14 <= |v| <= 65280 (every
+ *   bf16 value in fp16's normal range); below 2^-14 it truncates to an fp16 subnormal
+ *   (absolute error under 2^-24); |v| >= 65536 saturates to +-65504. PRECONDITION: the
+ *   latent dims (0..511) of every visible key row satisfy |v| <= 65280; larger values are
+ *   not detected, they saturate. The score dims (all 576) have no such limit.
  *
  * Conventions
  *   Ownership: every tensor argument is caller-owned device memory. The library owns the
  *     context and, only when the config brings no workspace, a workspace it allocates in
  *     verify_attn_create (outside any stream capture) and frees in verify_attn_destroy.
  *   Errors: functions return va_status; no exception or abort crosses the ABI. The message
- *     of the last failure on the calling thread is verify_attn_last_error().
+ *     of the last failure on the calling thread is verify_attn_last_error(). (The C-ABI
+ *     layer's job of type marshalling and error codes between the kernels and their
+ *     callers: "The Glue That Makes Kernels Run: A Study in Architectural Discipline",
+ *     section "The Subject Message: Why It Was Written"; "The Glue That Connects", section
+ *     "What the Edit Actually Does".)
  *   Bad device data (a slot outside [0, num_slots), L_r < T_r, T_r above max_q_per_req,
  *     offsets outside the buffers) never leads to an out-of-bounds access: the offending
  *     key is treated as invisible or the request's rows are written as empty rows, and a
@@ -176,7 +186,10 @@ va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_bu
                           int32_t *out_argmax, void *stream);
 
 /* Synchronises `stream`, returns the sticky VA_DEV_* bits in *flags and clears them.
- * Never call it inside a stream capture. */
+ * Never call it inside a stream capture. The hot path itself never synchronises or copies to
+ * the host ("The Final Solder Joint", sections "The Capture-Safety Constraint" and "Why the
+ * C-ABI Edit Matters"), so bad index data is reported through this separate, synchronising
+ * call rather than by verify_attn_run. Errors: VA_ERR_NULL, VA_ERR_HIP. */
 va_status verify_attn_read_device_status(verify_attn_ctx *ctx, void *stream, uint32_t *flags);
 
 /* Profiling: when set (non-NULL hipEvent_t handles passed as void*), every later
@@ -245,7 +258,9 @@ va_status verify_attn_accept(verify_attn_ctx *ctx, const int64_t *parents,
 /* Frees the context and any workspace it allocated. NULL is a no-op. */
 void verify_attn_destroy(verify_attn_ctx *ctx);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none; cleared by a successful call).
+ * Thread-local, owned by the library, valid until the thread's next call. The error-code
+ * convention it completes is cited under "Errors" above. */
 const char *verify_attn_last_error(void);
 
 #ifdef __cplusplus

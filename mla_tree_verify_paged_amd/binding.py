@@ -169,6 +169,85 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(name, t, dtypes, min_numel=0, shape=None, device_check=True):
+    """Raises ValueError unless `t` has one of `dtypes`, at least `min_numel` elements, the
+    given trailing shape (None entries match anything), is contiguous and (with
+    device_check) lives on a GPU. Shape and dtype are checked first."""
+    import torch
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _need(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+    if shape is not None:
+        _need(t.dim() == len(shape), f"{name} must have {len(shape)} dims, got {tuple(t.shape)}")
+        for i, (got, want) in enumerate(zip(t.shape, shape)):
+            _need(want is None or got == want,
+                  f"{name} dim {i} is {got}, expected {want} (shape {tuple(t.shape)})")
+    _need(t.numel() >= min_numel, f"{name} holds {t.numel()} elements, needs >= {min_numel}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if device_check:
+        _need(t.is_cuda, f"{name} must be a GPU tensor")
+
+
+def validate_run(num_heads, in_dtype, out_dtype, q, kv_buffer, kv_indices, kv_indptr,
+                 qo_indptr, custom_mask, mask_indptr, out, out_lse, out_argmax, bs, num_tokens,
+                 out_cache_loc=None, device_check=True):
+    """Checks the tensors of one verify step against the layouts include/verify_attn.h
+    states (dtype, shape, contiguity, device), so that no pointer reaches the C ABI with a
+    layout the kernels would misread. Raises ValueError."""
+    import torch
+    fdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
+    _need(bs >= 0 and num_tokens >= 0, "bs and num_tokens must be >= 0")
+    dc = device_check
+    _check_tensor("q", q, (fdt[in_dtype],), num_tokens * num_heads * 576,
+                  (None, num_heads, 576), dc)
+    _check_tensor("kv_buffer", kv_buffer, (fdt[in_dtype],), 576, (None, 576), dc)
+    _check_tensor("kv_indices", kv_indices, (torch.int64,), 0, None, dc)
+    _check_tensor("kv_indptr", kv_indptr, (torch.int32,), bs + 1, None, dc)
+    _check_tensor("qo_indptr", qo_indptr, (torch.int64,), bs + 1, None, dc)
+    _check_tensor("custom_mask", custom_mask, (torch.uint8, torch.bool), 0, None, dc)
+    _check_tensor("mask_indptr", mask_indptr, (torch.int64,), bs + 1, None, dc)
+    if out_cache_loc is not None:
+        _check_tensor("out_cache_loc", out_cache_loc, (torch.int64,), num_tokens, None, dc)
+    _check_tensor("out", out, (fdt[out_dtype],), num_tokens * num_heads * 512,
+                  (None, num_heads, 512), dc)
+    if out_lse is not None:
+        _check_tensor("out_lse", out_lse, (torch.float32,), num_tokens * num_heads, None, dc)
+    if out_argmax is not None:
+        _check_tensor("out_argmax", out_argmax, (torch.int32,), num_tokens * num_heads, None,
+                      dc)
+
+
+def validate_tree_args(parents, qo_indptr, kv_indptr, bs, num_tokens, custom_mask=None,
+                       mask_indptr=None, draft_tokens=None, target_tokens=None, accept_len=None,
+                       accept_path=None, next_token=None, device_check=True):
+    """The same checks for the mask build and the acceptance calls."""
+    import torch
+    dc = device_check
+    _need(bs >= 0 and num_tokens >= 0, "bs and num_tokens must be >= 0")
+    _check_tensor("parents", parents, (torch.int64,), num_tokens, None, dc)
+    _check_tensor("qo_indptr", qo_indptr, (torch.int64,), bs + 1, None, dc)
+    if kv_indptr is not None:
+        _check_tensor("kv_indptr", kv_indptr, (torch.int32,), bs + 1, None, dc)
+    if custom_mask is not None:
+        _check_tensor("custom_mask", custom_mask, (torch.uint8, torch.bool), 0, None, dc)
+    if mask_indptr is not None:
+        _check_tensor("mask_indptr", mask_indptr, (torch.int64,), bs + 1, None, dc)
+    for name, t in (("draft_tokens", draft_tokens), ("target_tokens", target_tokens)):
+        if t is not None:
+            _check_tensor(name, t, (torch.int64,), num_tokens, None, dc)
+    if accept_len is not None:
+        _check_tensor("accept_len", accept_len, (torch.int32,), bs, None, dc)
+    if accept_path is not None:
+        _check_tensor("accept_path", accept_path, (torch.int64,), bs, (None, None), dc)
+        _need(accept_path.shape[0] >= bs, "accept_path needs bs rows")
+    if next_token is not None:
+        _check_tensor("next_token", next_token, (torch.int64,), bs, None, dc)
+
+
 class VerifyAttn:
     """Owns one context; ``run`` marshals torch tensors into ``verify_attn_run``."""
 
@@ -193,6 +272,7 @@ class VerifyAttn:
         self.ctx = verify_attn_create(self.cfg)
         self.info = verify_attn_get_info(self.ctx)
         self.num_heads = num_heads
+        self.in_dtype = in_dtype
         self.out_dtype = out_dtype
 
     def run(self, q, kv_buffer, kv_indices, kv_indptr, qo_indptr, custom_mask, mask_indptr,
@@ -205,6 +285,9 @@ class VerifyAttn:
             bs = kv_indptr.numel() - 1
         if num_tokens is None:
             num_tokens = q.shape[0]
+        validate_run(self.num_heads, self.in_dtype, self.out_dtype, q, kv_buffer, kv_indices,
+                     kv_indptr, qo_indptr, custom_mask, mask_indptr, out, out_lse, out_argmax,
+                     int(bs), int(num_tokens), out_cache_loc)
         verify_attn_run(self.ctx, _ptr(q), _ptr(kv_buffer), kv_buffer.shape[0], _ptr(kv_indices),
                         kv_indices.numel(), _ptr(kv_indptr), _ptr(qo_indptr), _ptr(custom_mask),
                         custom_mask.numel(), _ptr(mask_indptr), _ptr(out_cache_loc), int(bs),
@@ -224,6 +307,8 @@ class VerifyAttn:
             bs = qo_indptr.numel() - 1
         if num_tokens is None:
             num_tokens = parents.numel()
+        validate_tree_args(parents, qo_indptr, kv_indptr, int(bs), int(num_tokens),
+                           custom_mask=custom_mask, mask_indptr=mask_indptr)
         verify_attn_build_mask(self.ctx, _ptr(parents), _ptr(qo_indptr), _ptr(kv_indptr),
                                int(bool(split_layout)), int(bs), int(num_tokens),
                                _ptr(custom_mask), custom_mask.numel(), _ptr(mask_indptr),
@@ -241,6 +326,9 @@ class VerifyAttn:
             bs = qo_indptr.numel() - 1
         if num_tokens is None:
             num_tokens = parents.numel()
+        validate_tree_args(parents, qo_indptr, None, int(bs), int(num_tokens),
+                           draft_tokens=draft_tokens, target_tokens=target_tokens,
+                           accept_len=accept_len, accept_path=accept_path, next_token=next_token)
         verify_attn_accept(self.ctx, _ptr(parents), _ptr(draft_tokens), _ptr(target_tokens),
                            _ptr(qo_indptr), int(bs), int(num_tokens), _ptr(accept_len),
                            _ptr(accept_path), int(accept_path.shape[1]), _ptr(next_token),

@@ -80,7 +80,8 @@ __global__ void __launch_bounds__(kMaskThreads) build_mask_kernel(TreeArgs a) {
   int32_t T, L, P;
   bool ok = a.bs > 0 && tree_shape(a, lo, q0, T, L, P) && t >= q0 && t < q0 + T;
   const int64_t m0 = ok ? a.mask_indptr[lo] : 0;
-  if (ok && (m0 < 0 || m0 + int64_t(T) * L > a.mask_len)) ok = false;
+  // (T <= 2048 and L <= INT32_MAX: T * L cannot overflow, nor can mask_len - T * L)
+  if (ok && (m0 < 0 || m0 > a.mask_len - int64_t(T) * L)) ok = false;
   if (!ok) {
     if (threadIdx.x == 0) atomicOr(a.status, 2u);  // VA_DEV_SEGMENT: row not written
     return;

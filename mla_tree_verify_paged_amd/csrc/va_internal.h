@@ -127,9 +127,11 @@ __device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segmen
   // the split layout: kv_indices holds the prefix, out_cache_loc[q0 .. q1) the tree slots
   const int64_t L = a.out_cache_loc ? n + T : n;
   s.T = 0; s.L = 0; s.P = 0;
+  // (T <= num_tokens < 2^26 and L <= INT32_MAX, so T * L cannot overflow; the mask bound is
+  // tested as m0 > mask_len - T * L, which cannot overflow either, whatever m0 holds)
   if (T < 0 || n < 0 || q0 < 0 || q1 > a.num_tokens || k0 < 0 || k1 > a.num_kv_indices ||
-      L < T || L > INT32_MAX || m0 < 0 || (T > 0 && m0 + T * L > a.mask_len) ||
-      T * L > INT32_MAX)
+      L < T || L > INT32_MAX || m0 < 0 || T * L > INT32_MAX ||
+      (T > 0 && m0 > a.mask_len - T * L))
     return 2u;  // VA_DEV_SEGMENT (a request's mask segment must stay under 2 GiB)
   if (T > a.max_q_per_req) return 4u;  // VA_DEV_Q_PER_REQ
   s.T = int32_t(T);
