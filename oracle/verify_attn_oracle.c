@@ -218,3 +218,129 @@ int oracle_verify_attn_f64(const void *q, const void *kv_buffer, int32_t in_dtyp
   }
   return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
 }
+
+/*
+ * Score diagnostics for checking an argmax computed in lower precision (same inputs, same
+ * tables, same visibility rule and score definition as oracle_verify_attn_f64).
+ *
+ * For each listed row (flat id t*H + h; every row when rows == NULL):
+ *   top1[n]   = m1 = the largest visible score s_j (-inf when no key is visible)
+ *   arg1[n]   = the smallest visible key position attaining m1 (-1 when none)
+ *   top2[n]   = the largest visible score among keys j != arg1[n] (-inf when none); it equals
+ *               m1 when the maximum is attained twice
+ *   absmax[n] = the largest visible |scale| * sum_d |q[t,h,d] * kv[slot_j,d]|, the magnitude
+ *               that bounds the rounding error of any summation order of s_j
+ * For each (row, key position) pair listed in pair_rows / pair_keys:
+ *   pair_s[p]   = s_j, and pair_abs[p] = |scale| * sum_d |q[t,h,d] kv[slot_j,d]|
+ *   pair_vis[p] = 1 if key j is visible to the row, else 0 (key positions outside [0, L_r)
+ *                 report 0 and NaN scores).
+ * Returns ORACLE_OK or ORACLE_ERR_INVALID / ORACLE_ERR_NOMEM.
+ */
+static void row_owner(const int64_t *qo_indptr, int32_t bs, int64_t t, int32_t *r) {
+  int32_t k = 0;
+  while (k + 1 < bs && qo_indptr[k + 1] <= t) ++k;
+  *r = k;
+}
+
+/* s_j and its magnitude bound for one (token t, head h, request r, key j). */
+static void key_score(const void *q, const void *kv_buffer, int32_t in_dtype,
+                      const int64_t *kv_indices, const int32_t *kv_indptr,
+                      const int64_t *qo_indptr, const int64_t *out_cache_loc, int32_t r,
+                      int64_t P, int64_t t, int64_t h, int32_t H, int64_t D, double scale,
+                      int64_t j, double *s, double *sabs) {
+  const int64_t qrow = (t * H + h) * D;
+  const int64_t krow = slot_of(kv_indices, kv_indptr, qo_indptr, out_cache_loc, r, P, j) * D;
+  double dot = 0.0, mag = 0.0;
+  for (int64_t e = 0; e < D; e++) {
+    const double p = elem(q, in_dtype, qrow + e) * elem(kv_buffer, in_dtype, krow + e);
+    dot += p;
+    mag += fabs(p);
+  }
+  *s = scale * dot;
+  *sabs = fabs(scale) * mag;
+}
+
+int oracle_score_top2_f64(const void *q, const void *kv_buffer, int32_t in_dtype,
+                          int64_t num_slots, const int64_t *kv_indices,
+                          const int32_t *kv_indptr, const int64_t *qo_indptr,
+                          const int64_t *out_cache_loc, const uint8_t *custom_mask,
+                          const int64_t *mask_indptr, int64_t mask_len, int32_t bs, int32_t H,
+                          int32_t Dl, int32_t Dr, double scale, const int64_t *rows,
+                          int64_t n_rows, double *top1, int64_t *arg1, double *top2,
+                          double *absmax, const int64_t *pair_rows, const int64_t *pair_keys,
+                          int64_t n_pairs, double *pair_s, double *pair_abs, int32_t *pair_vis,
+                          int32_t nthreads) {
+  if (in_dtype != ORACLE_BF16 && in_dtype != ORACLE_FP32) return ORACLE_ERR_INVALID;
+  if (bs < 0 || H < 1 || Dl < 1 || Dr < 0 || n_pairs < 0) return ORACLE_ERR_INVALID;
+  int rc = check_tables(num_slots, kv_indices, kv_indptr, qo_indptr, out_cache_loc, mask_indptr,
+                        mask_len, bs);
+  if (rc != ORACLE_OK) return rc;
+  const int64_t D = (int64_t)Dl + Dr;
+  const int64_t num_tokens = bs > 0 ? qo_indptr[bs] : 0;
+  const int64_t total = rows ? n_rows : num_tokens * H;
+  for (int64_t n = 0; n < total; ++n) {
+    const int64_t row = rows ? rows[n] : n;
+    if (row < 0 || row >= num_tokens * H) return ORACLE_ERR_INVALID;
+  }
+  for (int64_t p = 0; p < n_pairs; ++p)
+    if (pair_rows[p] < 0 || pair_rows[p] >= num_tokens * H) return ORACLE_ERR_INVALID;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int64_t n = 0; n < total; ++n) {
+    const int64_t row = rows ? rows[n] : n;
+    const int64_t t = row / H, h = row % H;
+    int32_t r;
+    row_owner(qo_indptr, bs, t, &r);
+    const int64_t i = t - qo_indptr[r];
+    const int64_t T = qo_indptr[r + 1] - qo_indptr[r];
+    const int64_t L = req_keys(kv_indptr, qo_indptr, out_cache_loc, r);
+    const int64_t P = L - T;
+    const uint8_t *mrow = custom_mask + mask_indptr[r] + i * L;
+    double m1 = -INFINITY, m2 = -INFINITY, amag = 0.0;
+    int64_t j1 = -1;
+    for (int64_t j = 0; j < L; ++j) {
+      if (!(j < P || mrow[j] != 0)) continue;
+      double s, sabs;
+      key_score(q, kv_buffer, in_dtype, kv_indices, kv_indptr, qo_indptr, out_cache_loc, r, P,
+                t, h, H, D, scale, j, &s, &sabs);
+      if (sabs > amag) amag = sabs;
+      if (s > m1) {
+        m2 = m1;
+        m1 = s;
+        j1 = j;
+      } else if (s > m2) {
+        m2 = s;
+      }
+    }
+    top1[n] = m1;
+    arg1[n] = j1;
+    top2[n] = m2;
+    absmax[n] = amag;
+  }
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+  for (int64_t p = 0; p < n_pairs; ++p) {
+    const int64_t t = pair_rows[p] / H, h = pair_rows[p] % H;
+    int32_t r;
+    row_owner(qo_indptr, bs, t, &r);
+    const int64_t i = t - qo_indptr[r];
+    const int64_t T = qo_indptr[r + 1] - qo_indptr[r];
+    const int64_t L = req_keys(kv_indptr, qo_indptr, out_cache_loc, r);
+    const int64_t P = L - T;
+    const int64_t j = pair_keys[p];
+    if (j < 0 || j >= L) {
+      pair_s[p] = NAN;
+      pair_abs[p] = NAN;
+      pair_vis[p] = 0;
+      continue;
+    }
+    const uint8_t *mrow = custom_mask + mask_indptr[r] + i * L;
+    pair_vis[p] = (j < P || mrow[j] != 0) ? 1 : 0;
+    key_score(q, kv_buffer, in_dtype, kv_indices, kv_indptr, qo_indptr, out_cache_loc, r, P, t,
+              h, H, D, scale, j, &pair_s[p], &pair_abs[p]);
+  }
+  return ORACLE_OK;
+}

@@ -38,7 +38,7 @@ def test_short_split(kernel):
     got = both_layouts(w, kernel)
     rows = sample_rows(w, 256, seed=3)
     ref = run_oracle(w, rows=rows, split=True)
-    compare(w, got, ref, rows=rows)
+    compare(w, got, ref, rows=rows, split=True)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
@@ -48,7 +48,7 @@ def test_segmented_split(kernel):
     got = both_layouts(w, kernel)
     rows = sample_rows(w, 256, seed=4)
     ref = run_oracle(w, rows=rows, split=True)
-    compare(w, got, ref, rows=rows)
+    compare(w, got, ref, rows=rows, split=True)
 
 
 def test_stress_split_mfma():
@@ -57,7 +57,7 @@ def test_stress_split_mfma():
     got = both_layouts(w, "mfma")
     rows = sample_rows(w, 64, seed=5, must=stress_depth8_rows(w)[:16])
     ref = run_oracle(w, rows=rows, split=True)
-    compare(w, got, ref, rows=rows)
+    compare(w, got, ref, rows=rows, split=True)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
