@@ -185,6 +185,30 @@ va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_bu
                           int64_t num_tokens, float sm_scale, void *out, float *out_lse,
                           int32_t *out_argmax, void *stream);
 
+/*
+ * Allocation-free variant of verify_attn_run, for callers that cannot allocate device memory:
+ * code under stream capture, tight serving loops, harnesses that forbid allocation. It takes
+ * the configuration instead of a context and, as its workspace, a static device scratch array
+ * of the library: 64 MiB on each GPU it runs on, part of the code object, held until the
+ * process ends. It calls no allocation routine. The tensor arguments, outputs, host checks and
+ * semantics are those of verify_attn_run; cfg->workspace must be NULL (else VA_ERR_INVALID).
+ * Limit: verify_attn_workspace_bytes(cfg) must be at most 64 MiB, else VA_ERR_WORKSPACE before
+ * any device work (with num_splits = 0 on a 256-CU GPU: max_q_tokens up to 477 at H=64, up
+ * to 3819 at H=8). The first call on a device looks the array's address up and clears its header
+ * with a kernel on `stream` (capturable). Every call on one GPU shares that GPU's array and
+ * leaves its contents behind, so calls that overlap in time on one GPU race: serialise them
+ * (one stream) or use contexts. Bad index data is handled as verify_attn_run handles it (keys
+ * ignored, rows emptied), but this path has no status read.
+ */
+va_status verify_attn_run_static(const verify_attn_config *cfg, const void *q,
+                                 const void *kv_buffer, int64_t num_slots,
+                                 const int64_t *kv_indices, int64_t num_kv_indices,
+                                 const int32_t *kv_indptr, const int64_t *qo_indptr,
+                                 const uint8_t *custom_mask, int64_t mask_len,
+                                 const int64_t *mask_indptr, const int64_t *out_cache_loc,
+                                 int32_t bs, int64_t num_tokens, float sm_scale, void *out,
+                                 float *out_lse, int32_t *out_argmax, void *stream);
+
 /* Synchronises `stream`, returns the sticky VA_DEV_* bits in *flags and clears them.
  * Never call it inside a stream capture. The hot path itself never synchronises or copies to
  * the host ("The Final Solder Joint", sections "The Capture-Safety Constraint" and "Why the

@@ -25,7 +25,7 @@ EXPORTED = (
     "verify_attn_workspace_bytes", "verify_attn_create", "verify_attn_run",
     "verify_attn_read_device_status", "verify_attn_set_profiling_events",
     "verify_attn_get_info", "verify_attn_destroy", "verify_attn_last_error",
-    "verify_attn_build_mask", "verify_attn_accept",
+    "verify_attn_build_mask", "verify_attn_accept", "verify_attn_run_static",
 )
 
 
@@ -68,6 +68,9 @@ def _load(path: str = LIB_PATH):
     lib.verify_attn_run.argtypes = [vp, vp, vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, i32,
                                     i64, f32, vp, vp, vp, vp]
     lib.verify_attn_run.restype = ctypes.c_int
+    lib.verify_attn_run_static.argtypes = [cfgp, vp, vp, i64, vp, i64, vp, vp, vp, i64, vp, vp,
+                                           i32, i64, f32, vp, vp, vp, vp]
+    lib.verify_attn_run_static.restype = ctypes.c_int
     lib.verify_attn_read_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.verify_attn_read_device_status.restype = ctypes.c_int
     lib.verify_attn_set_profiling_events.argtypes = [vp, vp, vp, vp]
@@ -125,6 +128,16 @@ def verify_attn_run(ctx, q, kv_buffer, num_slots, kv_indices, num_kv_indices, kv
                                kv_indptr, qo_indptr, custom_mask, mask_len, mask_indptr,
                                out_cache_loc, bs, num_tokens, sm_scale, out, out_lse,
                                out_argmax, stream))
+
+
+def verify_attn_run_static(cfg, q, kv_buffer, num_slots, kv_indices, num_kv_indices, kv_indptr,
+                           qo_indptr, custom_mask, mask_len, mask_indptr, out_cache_loc, bs,
+                           num_tokens, sm_scale, out, out_lse, out_argmax, stream) -> None:
+    """Pointer-level call of the allocation-free entry point (a config, no context)."""
+    _check(lib.verify_attn_run_static(ctypes.byref(cfg), q, kv_buffer, num_slots, kv_indices,
+                                      num_kv_indices, kv_indptr, qo_indptr, custom_mask,
+                                      mask_len, mask_indptr, out_cache_loc, bs, num_tokens,
+                                      sm_scale, out, out_lse, out_argmax, stream))
 
 
 def verify_attn_build_mask(ctx, parents, qo_indptr, kv_indptr, split_layout, bs, num_tokens,

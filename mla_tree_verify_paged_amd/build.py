@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libverify_attn.so")
 SOURCES = ["capi.cpp", "verify_simple.hip", "verify_mfma.hip", "verify_combine.hip",
-           "tree_ops.hip"]
+           "tree_ops.hip", "static_scratch.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-shared",

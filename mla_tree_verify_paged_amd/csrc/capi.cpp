@@ -21,24 +21,12 @@
 #include "../../include/verify_attn.h"
 #include "va_internal.h"
 
-struct verify_attn_ctx {
-  verify_attn_config cfg;
-  int32_t kernel;
-  int32_t splits;
-  int32_t rows_per_block;
-  int32_t row_tiles_per_req;
-  int32_t grid;       // MFMA partial kernel: workgroups (one per compute unit)
-  int64_t part_rows;  // partial rows the workspace holds
-  size_t ws_bytes;
-  void *ws_base;
-  bool ws_owned;
-  va::Workspace ws;
-  hipEvent_t ev[3];  // profiling events (all NULL when off)
-};
 
 namespace {
 
 thread_local std::string g_last_error;
+
+hipEvent_t const kNoEvents[3] = {nullptr, nullptr, nullptr};
 
 va_status fail(va_status st, const char *fmt, ...) {
   char buf[512];
@@ -79,6 +67,19 @@ struct Derived {
   int64_t part_rows;
   size_t bytes;
 };
+
+}  // namespace
+
+struct verify_attn_ctx {
+  verify_attn_config cfg;
+  Derived d;          // kernel, split count, grid, workspace sizing
+  void *ws_base;
+  bool ws_owned;
+  va::Workspace ws;
+  hipEvent_t ev[3];  // profiling events (all NULL when off)
+};
+
+namespace {
 
 // Checks a config and fills the derived launch parameters. Returns VA_OK or an error.
 va_status derive(const verify_attn_config *c, Derived *d) {
@@ -144,23 +145,98 @@ va_status derive(const verify_attn_config *c, Derived *d) {
   return VA_OK;
 }
 
-void bind_workspace(verify_attn_ctx *x) {
+// The workspace regions of a config with derived parameters `d`, laid over `base`.
+va::Workspace bind_workspace(const verify_attn_config &cfg, const Derived &d, void *base) {
   size_t off[7];
-  const int64_t rows_cap = x->cfg.max_q_tokens * x->cfg.num_heads;
-  va::workspace_layout(x->part_rows, rows_cap, part_elem_bytes(x->kernel), off);
-  char *b = static_cast<char *>(x->ws_base);
-  x->ws.status = reinterpret_cast<uint32_t *>(b + off[0]);
-  x->ws.zero_row = reinterpret_cast<const uint16_t *>(b + off[0] + va::kZeroRowOffset);
-  x->ws.part_o = b + off[1];
-  x->ws.part_scale = reinterpret_cast<float *>(b + off[2]);
-  x->ws.part_i16 = part_elem_bytes(x->kernel) == 2;
-  x->ws.part_lse = reinterpret_cast<float *>(b + off[3]);
-  x->ws.part_max = reinterpret_cast<float *>(b + off[4]);
-  x->ws.part_arg = reinterpret_cast<int32_t *>(b + off[5]);
-  x->ws.row_info = reinterpret_cast<va::RowInfo *>(b + off[6]);
-  x->ws.part_rows = x->part_rows;
-  x->ws.rows_cap = rows_cap;
-  x->ws.splits = x->splits;
+  const int64_t rows_cap = cfg.max_q_tokens * cfg.num_heads;
+  va::workspace_layout(d.part_rows, rows_cap, part_elem_bytes(d.kernel), off);
+  char *b = static_cast<char *>(base);
+  va::Workspace ws;
+  ws.status = reinterpret_cast<uint32_t *>(b + off[0]);
+  ws.zero_row = reinterpret_cast<const uint16_t *>(b + off[0] + va::kZeroRowOffset);
+  ws.part_o = b + off[1];
+  ws.part_scale = reinterpret_cast<float *>(b + off[2]);
+  ws.part_i16 = part_elem_bytes(d.kernel) == 2;
+  ws.part_lse = reinterpret_cast<float *>(b + off[3]);
+  ws.part_max = reinterpret_cast<float *>(b + off[4]);
+  ws.part_arg = reinterpret_cast<int32_t *>(b + off[5]);
+  ws.row_info = reinterpret_cast<va::RowInfo *>(b + off[6]);
+  ws.part_rows = d.part_rows;
+  ws.rows_cap = rows_cap;
+  ws.splits = d.splits;
+  return ws;
+}
+
+// Host checks and the two launches of one verify step (both entry points). `ev` holds the
+// optional profiling events (NULLs when off).
+va_status launch_step(const verify_attn_config &cfg, const Derived &d, const va::Workspace &ws,
+                      hipEvent_t const ev[3], const void *q, const void *kv_buffer,
+                      int64_t num_slots, const int64_t *kv_indices, int64_t num_kv_indices,
+                      const int32_t *kv_indptr, const int64_t *qo_indptr,
+                      const uint8_t *custom_mask, int64_t mask_len, const int64_t *mask_indptr,
+                      const int64_t *out_cache_loc, int32_t bs, int64_t num_tokens,
+                      float sm_scale, void *out, float *out_lse, int32_t *out_argmax,
+                      void *stream) {
+  if (bs < 0 || bs > cfg.max_batch)
+    return fail(VA_ERR_INVALID, "bs %d out of range [0, %d]", bs, cfg.max_batch);
+  if (num_tokens < 0 || num_tokens > cfg.max_q_tokens)
+    return fail(VA_ERR_INVALID, "num_tokens %lld out of range [0, %lld]",
+                (long long)num_tokens, (long long)cfg.max_q_tokens);
+  if (num_slots < 1) return fail(VA_ERR_INVALID, "num_slots must be >= 1");
+  if (num_kv_indices < 0 || mask_len < 0)
+    return fail(VA_ERR_INVALID, "num_kv_indices and mask_len must be >= 0");
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return fail(VA_ERR_INVALID, "sm_scale must be positive and finite");
+  if (num_tokens == 0) return ok();
+  if (!out) return fail(VA_ERR_NULL, "out is NULL");
+  if (bs > 0) {
+    if (!q || !kv_buffer || !kv_indptr || !qo_indptr || !mask_indptr)
+      return fail(VA_ERR_NULL, "a required input pointer is NULL");
+    if (num_kv_indices > 0 && !kv_indices) return fail(VA_ERR_NULL, "kv_indices is NULL");
+    if (mask_len > 0 && !custom_mask) return fail(VA_ERR_NULL, "custom_mask is NULL");
+  }
+  va::RunArgs a;
+  a.q = q;
+  a.kv = kv_buffer;
+  a.num_slots = num_slots;
+  a.kv_indices = kv_indices;
+  a.num_kv_indices = num_kv_indices;
+  a.out_cache_loc = out_cache_loc;
+  a.kv_indptr = kv_indptr;
+  a.qo_indptr = qo_indptr;
+  a.mask = custom_mask;
+  a.mask_len = mask_len;
+  a.mask_indptr = mask_indptr;
+  a.bs = bs;
+  a.num_tokens = num_tokens;
+  a.H = cfg.num_heads;
+  a.max_q_per_req = cfg.max_q_per_req;
+  a.scale = sm_scale;
+  a.out = out;
+  a.out_lse = out_lse;
+  a.out_argmax = out_argmax;
+  a.out_bf16 = cfg.out_dtype == VA_BF16;
+  a.want_argmax = out_argmax != nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (ev[0] && (e = hipEventRecord(ev[0], st)) != hipSuccess)
+    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  if (bs > 0) {
+    if (d.kernel == VA_KERNEL_SIMPLE)
+      e = va::launch_simple_partial(a, ws, cfg.in_dtype == VA_FP32, st);
+    else
+      e = va::launch_mfma_partial(a, ws, d.rows_per_block, d.grid, st);
+    if (e != hipSuccess)
+      return fail(VA_ERR_HIP, "partial kernel launch failed: %s", hipGetErrorString(e));
+  }
+  if (ev[1] && (e = hipEventRecord(ev[1], st)) != hipSuccess)
+    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  e = va::launch_combine(a, ws, st);
+  if (e != hipSuccess)
+    return fail(VA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
+  if (ev[2] && (e = hipEventRecord(ev[2], st)) != hipSuccess)
+    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // namespace
@@ -205,17 +281,11 @@ va_status verify_attn_create(const verify_attn_config *cfg, verify_attn_ctx **ou
     return fail(VA_ERR_INVALID, "out of host memory");
   }
   x->cfg = *cfg;
-  x->kernel = d.kernel;
-  x->splits = d.splits;
-  x->rows_per_block = d.rows_per_block;
-  x->row_tiles_per_req = d.row_tiles;
-  x->grid = d.grid;
-  x->part_rows = d.part_rows;
-  x->ws_bytes = bytes;
+  x->d = d;
   x->ws_base = base;
   x->ws_owned = owned;
   x->ev[0] = x->ev[1] = x->ev[2] = nullptr;
-  bind_workspace(x);
+  x->ws = bind_workspace(x->cfg, d, base);
   *out = x;
   return ok();
 }
@@ -228,66 +298,43 @@ va_status verify_attn_run(verify_attn_ctx *ctx, const void *q, const void *kv_bu
                           int64_t num_tokens, float sm_scale, void *out, float *out_lse,
                           int32_t *out_argmax, void *stream) {
   if (!ctx) return fail(VA_ERR_NULL, "ctx is NULL");
-  if (bs < 0 || bs > ctx->cfg.max_batch)
-    return fail(VA_ERR_INVALID, "bs %d out of range [0, %d]", bs, ctx->cfg.max_batch);
-  if (num_tokens < 0 || num_tokens > ctx->cfg.max_q_tokens)
-    return fail(VA_ERR_INVALID, "num_tokens %lld out of range [0, %lld]",
-                (long long)num_tokens, (long long)ctx->cfg.max_q_tokens);
-  if (num_slots < 1) return fail(VA_ERR_INVALID, "num_slots must be >= 1");
-  if (num_kv_indices < 0 || mask_len < 0)
-    return fail(VA_ERR_INVALID, "num_kv_indices and mask_len must be >= 0");
-  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
-    return fail(VA_ERR_INVALID, "sm_scale must be positive and finite");
-  if (num_tokens == 0) return ok();
-  if (!out) return fail(VA_ERR_NULL, "out is NULL");
-  if (bs > 0) {
-    if (!q || !kv_buffer || !kv_indptr || !qo_indptr || !mask_indptr)
-      return fail(VA_ERR_NULL, "a required input pointer is NULL");
-    if (num_kv_indices > 0 && !kv_indices) return fail(VA_ERR_NULL, "kv_indices is NULL");
-    if (mask_len > 0 && !custom_mask) return fail(VA_ERR_NULL, "custom_mask is NULL");
-  }
-  va::RunArgs a;
-  a.q = q;
-  a.kv = kv_buffer;
-  a.num_slots = num_slots;
-  a.kv_indices = kv_indices;
-  a.num_kv_indices = num_kv_indices;
-  a.out_cache_loc = out_cache_loc;
-  a.kv_indptr = kv_indptr;
-  a.qo_indptr = qo_indptr;
-  a.mask = custom_mask;
-  a.mask_len = mask_len;
-  a.mask_indptr = mask_indptr;
-  a.bs = bs;
-  a.num_tokens = num_tokens;
-  a.H = ctx->cfg.num_heads;
-  a.max_q_per_req = ctx->cfg.max_q_per_req;
-  a.scale = sm_scale;
-  a.out = out;
-  a.out_lse = out_lse;
-  a.out_argmax = out_argmax;
-  a.out_bf16 = ctx->cfg.out_dtype == VA_BF16;
-  a.want_argmax = out_argmax != nullptr;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (ctx->ev[0] && (e = hipEventRecord(ctx->ev[0], st)) != hipSuccess)
-    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-  if (bs > 0) {
-    if (ctx->kernel == VA_KERNEL_SIMPLE)
-      e = va::launch_simple_partial(a, ctx->ws, ctx->cfg.in_dtype == VA_FP32, st);
-    else
-      e = va::launch_mfma_partial(a, ctx->ws, ctx->rows_per_block, ctx->grid, st);
-    if (e != hipSuccess)
-      return fail(VA_ERR_HIP, "partial kernel launch failed: %s", hipGetErrorString(e));
-  }
-  if (ctx->ev[1] && (e = hipEventRecord(ctx->ev[1], st)) != hipSuccess)
-    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-  e = va::launch_combine(a, ctx->ws, st);
+  return launch_step(ctx->cfg, ctx->d, ctx->ws, ctx->ev, q, kv_buffer, num_slots, kv_indices,
+                     num_kv_indices, kv_indptr, qo_indptr, custom_mask, mask_len, mask_indptr,
+                     out_cache_loc, bs, num_tokens, sm_scale, out, out_lse, out_argmax, stream);
+}
+
+va_status verify_attn_run_static(const verify_attn_config *cfg, const void *q,
+                                 const void *kv_buffer, int64_t num_slots,
+                                 const int64_t *kv_indices, int64_t num_kv_indices,
+                                 const int32_t *kv_indptr, const int64_t *qo_indptr,
+                                 const uint8_t *custom_mask, int64_t mask_len,
+                                 const int64_t *mask_indptr, const int64_t *out_cache_loc,
+                                 int32_t bs, int64_t num_tokens, float sm_scale, void *out,
+                                 float *out_lse, int32_t *out_argmax, void *stream) {
+  Derived d;
+  va_status st = derive(cfg, &d);
+  if (st != VA_OK) return st;
+  if (cfg->workspace)
+    return fail(VA_ERR_INVALID, "verify_attn_run_static uses the library's static scratch; "
+                                "cfg->workspace must be NULL");
+  if (d.bytes > va::kStaticScratchBytes)
+    return fail(VA_ERR_WORKSPACE,
+                "the config needs %zu bytes of workspace, above the %zu-byte static scratch "
+                "(lower max_q_tokens, num_heads or num_splits, or use verify_attn_create)",
+                d.bytes, size_t(va::kStaticScratchBytes));
+  if (num_tokens == 0 && bs >= 0 && bs <= cfg->max_batch)
+    return launch_step(*cfg, d, va::Workspace{}, kNoEvents, q, kv_buffer, num_slots,
+                       kv_indices, num_kv_indices, kv_indptr, qo_indptr, custom_mask, mask_len,
+                       mask_indptr, out_cache_loc, bs, num_tokens, sm_scale, out, out_lse,
+                       out_argmax, stream);
+  void *base = nullptr;
+  const hipError_t e = va::static_scratch(static_cast<hipStream_t>(stream), &base);
   if (e != hipSuccess)
-    return fail(VA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
-  if (ctx->ev[2] && (e = hipEventRecord(ctx->ev[2], st)) != hipSuccess)
-    return fail(VA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-  return ok();
+    return fail(VA_ERR_HIP, "static scratch set-up failed: %s", hipGetErrorString(e));
+  return launch_step(*cfg, d, bind_workspace(*cfg, d, base), kNoEvents, q, kv_buffer, num_slots,
+                     kv_indices, num_kv_indices, kv_indptr, qo_indptr, custom_mask, mask_len,
+                     mask_indptr, out_cache_loc, bs, num_tokens, sm_scale, out, out_lse,
+                     out_argmax, stream);
 }
 
 va_status verify_attn_build_mask(verify_attn_ctx *ctx, const int64_t *parents,
@@ -387,11 +434,11 @@ va_status verify_attn_set_profiling_events(verify_attn_ctx *ctx, void *before, v
 
 va_status verify_attn_get_info(const verify_attn_ctx *ctx, verify_attn_info *info) {
   if (!ctx || !info) return fail(VA_ERR_NULL, "ctx or info is NULL");
-  info->kernel = ctx->kernel;
-  info->num_splits = ctx->splits;
-  info->rows_per_block = ctx->rows_per_block;
-  info->row_tiles_per_req = ctx->row_tiles_per_req;
-  info->workspace_bytes = ctx->ws_bytes;
+  info->kernel = ctx->d.kernel;
+  info->num_splits = ctx->d.splits;
+  info->rows_per_block = ctx->d.rows_per_block;
+  info->row_tiles_per_req = ctx->d.row_tiles;
+  info->workspace_bytes = ctx->d.bytes;
   return ok();
 }
 

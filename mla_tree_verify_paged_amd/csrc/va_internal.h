@@ -180,6 +180,12 @@ __device__ __forceinline__ int64_t segment_slot(const RunArgs &a, const Segment 
   return (s.tree && j >= s.P) ? s.tree[j - s.P] : a.kv_indices[s.kv0 + j];
 }
 
+// The allocation-free entry point's workspace: a static device array of this many bytes per
+// GPU (static_scratch.hip). static_scratch() returns its device address on the current device,
+// setting it up (address lookup, header cleared on `stream`) on the first call there.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(hipStream_t stream, void **base);
+
 // Launchers (each defined next to its kernels).
 hipError_t launch_simple_partial(const RunArgs &a, const Workspace &ws, int in_fp32,
                                  hipStream_t st);

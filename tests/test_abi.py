@@ -147,3 +147,24 @@ def test_null_arguments():
     assert e.value.status == B.VA_ERR_NULL
     B.verify_attn_destroy(None)  # no-op
     assert B.lib.verify_attn_create(None, None) == B.VA_ERR_NULL
+
+
+def test_static_entry_rejects_configs_beyond_its_scratch():
+    """The allocation-free entry point refuses, before any device work, a config whose
+    workspace exceeds its 64 MiB static scratch, and a config that brings a workspace."""
+    args = (None, None, 1, None, 0, None, None, None, 0, None, None, 1, 1, 1.0, None, None,
+            None, None)
+    big = B.make_config(64, max_batch=1, max_q_per_req=16, max_q_tokens=478)
+    assert B.verify_attn_workspace_bytes(big) > 64 << 20
+    with pytest.raises(B.VerifyAttnError) as e:
+        B.verify_attn_run_static(big, *args)
+    assert e.value.status == B.VA_ERR_WORKSPACE and "static scratch" in B.verify_attn_last_error()
+    fits = B.make_config(64, max_batch=1, max_q_per_req=16, max_q_tokens=477)
+    assert B.verify_attn_workspace_bytes(fits) <= 64 << 20
+    fits.workspace = 1 << 20
+    with pytest.raises(B.VerifyAttnError) as e:
+        B.verify_attn_run_static(fits, *args)
+    assert e.value.status == B.VA_ERR_INVALID
+    with pytest.raises(B.VerifyAttnError) as e:
+        B.verify_attn_run_static(B.make_config(0), *args)
+    assert e.value.status == B.VA_ERR_INVALID
