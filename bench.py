@@ -168,6 +168,38 @@ def time_tree_ops(w, va, steps):
             "timing": "back-to-back launches on torch's current stream, averaged"}
 
 
+def single_launch_ab(partial_us, combine_us, step_us):
+    """The fixed costs of a single-launch merge on this GPU (csrc/single_launch_ab.hip):
+    a cooperative launch and one grid barrier, against the measured two-launch step. The
+    fused step cannot take less than the partial kernel plus those two costs (its merge
+    reads the same partials the combine reads)."""
+    lib_path = os.path.join(ROOT, "mla_tree_verify_paged_amd", "libsingle_launch_ab.so")
+    lib = ctypes.CDLL(lib_path)
+    lib.single_launch_ab.argtypes = [ctypes.POINTER(ctypes.c_double)]
+    lib.single_launch_ab.restype = ctypes.c_int
+    out = (ctypes.c_double * 8)()
+    rc = lib.single_launch_ab(out)
+    if rc != 0:
+        return {"error": f"hip error {rc}"}
+    plain, coop, coop1, coop33, graph1, timeouts, mismatches, captured = list(out)
+    barrier_us = (coop33 - coop1) / 64.0          # 33 barrier pairs against 1
+    coop_overhead_us = coop - plain
+    bound = partial_us + coop_overhead_us + barrier_us
+    return {
+        "plain_launch_us": round(plain, 2), "cooperative_launch_us": round(coop, 2),
+        "cooperative_overhead_us": round(coop_overhead_us, 2),
+        "grid_barrier_us": round(barrier_us, 2),
+        "cooperative_graph_replay_1_barrier_pair_us": round(graph1, 2),
+        "cooperative_capture_ok": bool(captured), "barrier_timeouts": int(timeouts),
+        "visibility_mismatches": int(mismatches),
+        "two_launch_step_us": round(step_us, 2), "two_launch_combine_us": round(combine_us, 2),
+        "fused_step_lower_bound_us": round(bound, 2),
+        "fused_wins": bool(bound < step_us),
+        "method": "fused >= partial kernel + (cooperative - plain launch) + one grid barrier; "
+                  "1 vs 33 barrier pairs on 1 workgroup per CU with 150 KB LDS",
+    }
+
+
 def workload_names():
     import workloads
     return workloads.CONFIGS.keys()
@@ -186,6 +218,10 @@ def main():
                          "prefix-only kv_indices plus out_cache_loc")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=50)
+    ap.add_argument("--single-launch-ab", action="store_true",
+                    help="also measure the fixed costs a single-launch (fused) merge would pay: "
+                         "cooperative launch overhead and one grid barrier, against this step's "
+                         "two-launch time (extra key single_launch_ab)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one elementwise kernel that reads and writes 256 MiB (for "
                          "scaling hardware byte counters)")
@@ -301,6 +337,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    single_launch = None
+    if args.single_launch_ab:
+        single_launch = single_launch_ab(part_ms.mean() * 1e3, comb_ms.mean() * 1e3,
+                                         ms_per_step * 1e3)
+        log(f"single-launch A/B: {single_launch}")
+
     tree_ops = time_tree_ops(w, va, args.steps)
     log(f"tree ops: {tree_ops}")
 
@@ -363,6 +405,8 @@ def main():
         "tree_ops": tree_ops,
         "cpu_baseline": None,
     }
+    if single_launch is not None:
+        result["single_launch_ab"] = single_launch
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -32,6 +32,21 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+AB_SOURCE = "single_launch_ab.hip"  # a separate measurement library, not the verify library
+AB_LIB = os.path.join(HERE, "libsingle_launch_ab.so")
+
+
+def build_ab(verbose: bool = False) -> str:
+    """Builds the single-launch A/B measurement library (bench.py --single-launch-ab)."""
+    tmp = AB_LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, AB_SOURCE), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-8000:]}")
+    os.replace(tmp, AB_LIB)
+    return AB_LIB
+
+
 def build(verbose: bool = False, extra=()) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
@@ -49,3 +64,4 @@ def build(verbose: bool = False, extra=()) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_ab())
