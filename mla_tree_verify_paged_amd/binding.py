@@ -290,7 +290,10 @@ class VerifyAttn:
 
     def run(self, q, kv_buffer, kv_indices, kv_indptr, qo_indptr, custom_mask, mask_indptr,
             sm_scale, out, out_lse=None, out_argmax=None, bs=None, num_tokens=None, stream=None,
-            out_cache_loc=None):
+            out_cache_loc=None, check=True):
+        """One verify step. With check=False the tensor layout checks (validate_run) are
+        skipped: for callers that reuse buffers already checked once, since the checks cost
+        tens of microseconds of host time per call."""
         import torch
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
@@ -298,9 +301,10 @@ class VerifyAttn:
             bs = kv_indptr.numel() - 1
         if num_tokens is None:
             num_tokens = q.shape[0]
-        validate_run(self.num_heads, self.in_dtype, self.out_dtype, q, kv_buffer, kv_indices,
-                     kv_indptr, qo_indptr, custom_mask, mask_indptr, out, out_lse, out_argmax,
-                     int(bs), int(num_tokens), out_cache_loc)
+        if check:
+            validate_run(self.num_heads, self.in_dtype, self.out_dtype, q, kv_buffer, kv_indices,
+                         kv_indptr, qo_indptr, custom_mask, mask_indptr, out, out_lse,
+                         out_argmax, int(bs), int(num_tokens), out_cache_loc)
         verify_attn_run(self.ctx, _ptr(q), _ptr(kv_buffer), kv_buffer.shape[0], _ptr(kv_indices),
                         kv_indices.numel(), _ptr(kv_indptr), _ptr(qo_indptr), _ptr(custom_mask),
                         custom_mask.numel(), _ptr(mask_indptr), _ptr(out_cache_loc), int(bs),
@@ -310,7 +314,7 @@ class VerifyAttn:
 
     def build_mask(self, parents, qo_indptr, kv_indptr, custom_mask, mask_indptr,
                    split_layout=False, write_mask_indptr=True, bs=None, num_tokens=None,
-                   stream=None):
+                   stream=None, check=True):
         """Builds the verify mask from the tree parents into `custom_mask` (and, by default,
         writes `mask_indptr`)."""
         import torch
@@ -320,8 +324,9 @@ class VerifyAttn:
             bs = qo_indptr.numel() - 1
         if num_tokens is None:
             num_tokens = parents.numel()
-        validate_tree_args(parents, qo_indptr, kv_indptr, int(bs), int(num_tokens),
-                           custom_mask=custom_mask, mask_indptr=mask_indptr)
+        if check:
+            validate_tree_args(parents, qo_indptr, kv_indptr, int(bs), int(num_tokens),
+                               custom_mask=custom_mask, mask_indptr=mask_indptr)
         verify_attn_build_mask(self.ctx, _ptr(parents), _ptr(qo_indptr), _ptr(kv_indptr),
                                int(bool(split_layout)), int(bs), int(num_tokens),
                                _ptr(custom_mask), custom_mask.numel(), _ptr(mask_indptr),
@@ -329,7 +334,7 @@ class VerifyAttn:
         return custom_mask
 
     def accept(self, parents, draft_tokens, target_tokens, qo_indptr, accept_len, accept_path,
-               next_token, bs=None, num_tokens=None, stream=None):
+               next_token, bs=None, num_tokens=None, stream=None, check=True):
         """Greedy acceptance: fills accept_len [bs], accept_path [bs, max_path] and
         next_token [bs]."""
         import torch
@@ -339,9 +344,11 @@ class VerifyAttn:
             bs = qo_indptr.numel() - 1
         if num_tokens is None:
             num_tokens = parents.numel()
-        validate_tree_args(parents, qo_indptr, None, int(bs), int(num_tokens),
-                           draft_tokens=draft_tokens, target_tokens=target_tokens,
-                           accept_len=accept_len, accept_path=accept_path, next_token=next_token)
+        if check:
+            validate_tree_args(parents, qo_indptr, None, int(bs), int(num_tokens),
+                               draft_tokens=draft_tokens, target_tokens=target_tokens,
+                               accept_len=accept_len, accept_path=accept_path,
+                               next_token=next_token)
         verify_attn_accept(self.ctx, _ptr(parents), _ptr(draft_tokens), _ptr(target_tokens),
                            _ptr(qo_indptr), int(bs), int(num_tokens), _ptr(accept_len),
                            _ptr(accept_path), int(accept_path.shape[1]), _ptr(next_token),

@@ -10,13 +10,14 @@
 // draft token equals the target's token at the current node.
 //
 // Both are small integer kernels: every output is exact.
+#include <algorithm>
+
 #include "va_internal.h"
 
 namespace va {
 namespace {
 
 constexpr int kMaskThreads = 256;
-constexpr int kScanThreads = 256;
 
 // (T, L, P) of request r for either slot layout; false if the segment is not usable.
 __device__ __forceinline__ bool tree_shape(const TreeArgs &a, int r, int64_t &q0, int32_t &T,
@@ -35,40 +36,61 @@ __device__ __forceinline__ bool tree_shape(const TreeArgs &a, int r, int64_t &q0
   return true;
 }
 
-// mask_indptr[r+1] = sum over requests <= r of T_r * L_r (0 for an unusable request).
-__global__ void __launch_bounds__(kScanThreads) mask_indptr_kernel(TreeArgs a) {
-  __shared__ int64_t part[kScanThreads];
+// Segment length T_r * L_r of request r in the mask (0 for an unusable request).
+__device__ __forceinline__ int64_t mask_segment(const TreeArgs &a, int r) {
+  int64_t q0;
+  int32_t T, L, P;
+  return tree_shape(a, r, q0, T, L, P) ? int64_t(T) * L : 0;
+}
+
+// Sum of mask_segment over requests [0, r), by all threads of the workgroup.
+__device__ int64_t mask_offset(const TreeArgs &a, int r, int64_t *red) {
+  int64_t v = 0;
+  for (int k = int(threadIdx.x); k < r; k += kMaskThreads) v += mask_segment(a, k);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int64_t s = 0;
+#pragma unroll
+  for (int w = 0; w < kMaskThreads / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// mask_indptr[r+1] = sum over requests <= r of T_r * L_r (workgroup 0 of the mask build).
+__device__ void write_mask_indptr(const TreeArgs &a, int64_t *part) {
   int64_t carry = 0;
   if (threadIdx.x == 0) a.mask_indptr[0] = 0;
-  for (int base = 0; base < a.bs; base += kScanThreads) {
+  for (int base = 0; base < a.bs; base += kMaskThreads) {
     const int r = base + int(threadIdx.x);
-    int64_t v = 0;
-    if (r < a.bs) {
-      int64_t q0;
-      int32_t T, L, P;
-      if (tree_shape(a, r, q0, T, L, P)) v = int64_t(T) * L;
-    }
-    part[threadIdx.x] = v;
+    part[threadIdx.x] = r < a.bs ? mask_segment(a, r) : 0;
     __syncthreads();
     // inclusive scan (Hillis-Steele)
-    for (int o = 1; o < kScanThreads; o <<= 1) {
+    for (int o = 1; o < kMaskThreads; o <<= 1) {
       const int64_t x = threadIdx.x >= unsigned(o) ? part[threadIdx.x - o] : 0;
       __syncthreads();
       part[threadIdx.x] += x;
       __syncthreads();
     }
     if (r < a.bs) a.mask_indptr[r + 1] = carry + part[threadIdx.x];
-    carry += part[kScanThreads - 1];
+    carry += part[kMaskThreads - 1];
     __syncthreads();
   }
 }
 
-// One workgroup per mask row (tree token t).
+// The whole mask build in one launch: one workgroup per mask row (tree token t). With
+// write_indptr, each workgroup derives its row's segment offset itself (a reduction over the
+// requests before its own) and workgroup 0 also writes mask_indptr, so no separate scan
+// launch precedes the rows.
+template <bool kWriteIndptr>
 __global__ void __launch_bounds__(kMaskThreads) build_mask_kernel(TreeArgs a) {
   extern __shared__ int32_t tree_smem[];  // parents [max_q_per_req], then ancestor flags
+  __shared__ int64_t scan[kMaskThreads];
   int32_t *par = tree_smem;
   int32_t *anc = tree_smem + a.max_q_per_req;
   const int64_t t = blockIdx.x;
+  if (kWriteIndptr && blockIdx.x == 0) write_mask_indptr(a, scan);
   if (t >= a.num_tokens) return;
   // the request that owns token t: the last r with qo_indptr[r] <= t
   int lo = 0, hi = a.bs;
@@ -79,7 +101,12 @@ __global__ void __launch_bounds__(kMaskThreads) build_mask_kernel(TreeArgs a) {
   int64_t q0;
   int32_t T, L, P;
   bool ok = a.bs > 0 && tree_shape(a, lo, q0, T, L, P) && t >= q0 && t < q0 + T;
-  const int64_t m0 = ok ? a.mask_indptr[lo] : 0;
+  int64_t m0 = 0;
+  if (kWriteIndptr) {
+    m0 = mask_offset(a, ok ? lo : 0, scan);  // every thread of the workgroup takes part
+  } else if (ok) {
+    m0 = a.mask_indptr[lo];
+  }
   // (T <= 2048 and L <= INT32_MAX: T * L cannot overflow, nor can mask_len - T * L)
   if (ok && (m0 < 0 || m0 > a.mask_len - int64_t(T) * L)) ok = false;
   if (!ok) {
@@ -182,16 +209,17 @@ __global__ void __launch_bounds__(64) accept_kernel(AcceptArgs a) {
 }  // namespace
 
 hipError_t launch_build_mask(const TreeArgs &a, bool write_indptr, hipStream_t st) {
-  if (write_indptr) {
-    hipLaunchKernelGGL(mask_indptr_kernel, dim3(1), dim3(kScanThreads), 0, st, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.num_tokens <= 0) return hipSuccess;
   if (a.num_tokens > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // one workgroup per mask row; at least one to write mask_indptr when asked
+  const int64_t grid = std::max<int64_t>(a.num_tokens, write_indptr ? 1 : 0);
+  if (grid == 0) return hipSuccess;
   const size_t smem = size_t(2) * a.max_q_per_req * sizeof(int32_t);
-  hipLaunchKernelGGL(build_mask_kernel, dim3(unsigned(a.num_tokens)), dim3(kMaskThreads), smem,
-                     st, a);
+  if (write_indptr)
+    hipLaunchKernelGGL(build_mask_kernel<true>, dim3(unsigned(grid)), dim3(kMaskThreads), smem,
+                       st, a);
+  else
+    hipLaunchKernelGGL(build_mask_kernel<false>, dim3(unsigned(grid)), dim3(kMaskThreads), smem,
+                       st, a);
   return hipGetLastError();
 }
 

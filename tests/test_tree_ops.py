@@ -50,6 +50,26 @@ def test_build_mask_matches_oracle(name, split):
     assert np.array_equal(mask, w.custom_mask)  # the generator's own mask, built on the host
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_build_mask_many_requests(split):
+    """300 requests, some without tree tokens: the single-launch build reduces and scans the
+    segment lengths over more requests than one workgroup pass covers."""
+    rng = np.random.default_rng(70)
+    t = rng.integers(0, 6, 300)
+    p = rng.integers(0, 400, 300)
+    w = wl.build_workload("mask300", rng, 2, p, t, int((p + t).sum()) + 64)
+    parents = np.concatenate(w.parents) if w.num_tokens else np.zeros(0, np.int64)
+    kv = w.split_buffers()[1] if split else w.kv_indptr
+    ref_mask, ref_ind = to.build_mask(parents, w.qo_indptr, kv, split=split)
+    mask, ind, status = gpu_mask(w, split)
+    assert status == 0
+    assert np.array_equal(ind, ref_ind)
+    assert np.array_equal(mask, ref_mask)
+    # and with the offsets given instead of written
+    mask2, ind2, status2 = gpu_mask(w, split, indptr=ref_ind)
+    assert status2 == 0 and np.array_equal(mask2, ref_mask)
+
+
 def test_build_mask_reads_given_indptr():
     """Segments at caller-chosen offsets (with gaps): only the segments are written."""
     w = wl.segmented()
