@@ -102,28 +102,58 @@ class HipEvents:
         self.rt.hipEventDestroy(e)
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """The fp64 oracle on the host cores: a bounded, deterministic sample of rows, scaled to a
-    whole step."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_us_per_step(w, pool, cores, budget_s, reps=3):
+    """Median over `reps` runs of the oracle on an evenly spaced sample of the workload's
+    rows sized to about budget_s / reps seconds per run, scaled to all rows (us per step).
+    Returns (us_per_step, rows_in_sample, median_run_seconds)."""
     import oracle
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     total = w.num_tokens * w.num_heads
-    pool = w.pool_np()
-    probe = np.arange(0, total, max(1, total // 32))[:32]
+    probe = np.arange(0, total, max(1, total // 16))[:16]
     t0 = time.perf_counter()
     oracle.run_workload(w, rows=probe, nthreads=cores, pool=pool)
     per_row = (time.perf_counter() - t0) / len(probe)
-    n = int(min(total, max(len(probe), budget_s / max(per_row, 1e-9))))
-    rows = np.linspace(0, total - 1, n).round().astype(np.int64)
-    rows = np.unique(rows)
-    t0 = time.perf_counter()
-    oracle.run_workload(w, rows=rows, nthreads=cores, pool=pool)
-    dt = time.perf_counter() - t0
-    us_step = dt / len(rows) * total * 1e6
+    n = int(min(total, max(len(probe), budget_s / reps / max(per_row, 1e-9))))
+    rows = np.unique(np.linspace(0, total - 1, n).round().astype(np.int64))
+    runs = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.run_workload(w, rows=rows, nthreads=cores, pool=pool)
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
+    return dt / len(rows) * total * 1e6, len(rows), dt
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle on the host cores: a bounded, deterministic sample of rows of the
+    bench's workload (median of 3 runs, scaled to a whole step), plus single-threaded timings
+    of the tiny and short workloads."""
+    import workloads
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    total = w.num_tokens * w.num_heads
+    us_step, n_rows, dt = oracle_us_per_step(w, w.pool_np(), cores, budget_s)
+    single = {}
+    for name, budget in (("tiny", 0.3), ("short", 4.0)):
+        sw = workloads.make(name)
+        us, rows, sdt = oracle_us_per_step(sw, sw.pool_np(), 1, budget)
+        single[name] = {"us_per_step": round(us, 1), "rows_in_sample": rows,
+                        "rows_total": sw.num_tokens * sw.num_heads,
+                        "median_run_s": round(sdt, 3)}
     return {"value": us_step, "unit": "us/step", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} of {total} (token, head) rows of the same workload, evenly "
-                      f"spaced, fp64 two-pass C loop with OpenMP; {dt:.2f} s wall, scaled to "
-                      f"all rows"}
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{n_rows} of {total} (token, head) rows of the same workload, evenly "
+                      f"spaced; fp64 two-pass C loop with OpenMP on {cores} threads; median of "
+                      f"3 runs ({dt:.2f} s each), scaled to all rows",
+            "single_thread": single}
 
 
 def time_tree_ops(w, va, steps):
@@ -213,6 +243,101 @@ def single_launch_ab(partial_us, combine_us, step_us):
     }
 
 
+SWEEP_P = (1024, 5700, 23000, 65536, 131072)
+SWEEP_T = (1, 4, 16, 64)
+SWEEP_BS = (1, 8, 32)
+
+
+def sweep(heads=64, budget_s=0.2, seed=0):
+    """Step time over prefix length x tree size x batch size (H = 64, one GPU): where the path
+    is bound by HBM bytes and where by matrix work. Inputs are drawn on the device (seeded
+    standard normal bf16 q and key rows, key rows scattered over a pool with one ninth of its
+    slots unused, random draft trees per request whose mask the library's own mask build
+    writes); each case is captured in a graph and replayed."""
+    import torch
+    import workloads
+    from mla_tree_verify_paged_amd import VerifyAttn
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    out_rows = []
+    for P in SWEEP_P:
+        for T in SWEEP_T:
+            for bs in SWEEP_BS:
+                L = P + T
+                n_keys, n_tok = bs * L, bs * T
+                slots = n_keys + n_keys // 8
+                q = torch.randn((n_tok, heads, 576), generator=gen, device="cuda").bfloat16()
+                pool = torch.empty((slots, 576), dtype=torch.bfloat16, device="cuda")
+                for a in range(0, slots, 1 << 20):  # in chunks: bounded fp32 temporaries
+                    b = min(slots, a + (1 << 20))
+                    pool[a:b] = torch.randn((b - a, 576), generator=gen, device="cuda").bfloat16()
+                kvi = torch.randperm(slots, generator=gen, device="cuda")[:n_keys].contiguous()
+                kvp = (torch.arange(bs + 1, device="cuda", dtype=torch.int64) * L).int()
+                qo = torch.arange(bs + 1, device="cuda", dtype=torch.int64) * T
+                trees = [workloads.random_tree(T, rng) for _ in range(bs)]
+                par = torch.from_numpy(np.concatenate(trees)).cuda()
+                va = VerifyAttn(heads, max_batch=bs, max_q_per_req=T, max_q_tokens=n_tok)
+                mask = torch.empty(bs * T * L, dtype=torch.uint8, device="cuda")
+                mind = torch.empty(bs + 1, dtype=torch.int64, device="cuda")
+                va.build_mask(par, qo, kvp, mask, mind)
+                out = torch.empty((n_tok, heads, 512), dtype=torch.float32, device="cuda")
+                lse = torch.empty((n_tok, heads), dtype=torch.float32, device="cuda")
+
+                def step(check=False):
+                    va.run(q, pool, kvi, kvp, qo, mask, mind, workloads.DEFAULT_SCALE, out, lse,
+                           None, bs=bs, num_tokens=n_tok, check=check)
+
+                step(True)
+                torch.cuda.synchronize()
+                status = va.read_device_status()
+                g = torch.cuda.CUDAGraph()
+                st = torch.cuda.Stream()
+                st.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(st):
+                    step()
+                torch.cuda.current_stream().wait_stream(st)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g):
+                    step()
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev1 = torch.cuda.Event(enable_timing=True)
+                g.replay()
+                ev0.record()
+                g.replay()
+                ev1.record()
+                ev1.synchronize()
+                est = ev0.elapsed_time(ev1) * 1e-3
+                reps = int(min(50, max(3, budget_s / max(est, 1e-6))))
+                ev0.record()
+                for _ in range(reps):
+                    g.replay()
+                ev1.record()
+                ev1.synchronize()
+                us = ev0.elapsed_time(ev1) * 1e3 / reps
+                vis = sum(int(workloads.tree_depths(t).sum()) + T for t in trees)
+                fl = 2 * (576 + 512) * heads * (bs * T * P + vis)
+                by = bs * (L * (576 * 2 + 8) + T * heads * (576 * 2 + 512 * 4) + T * T) + \
+                    (bs + 1) * 20
+                f_mfma = fl / (us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS
+                f_hbm = by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS
+                hbm_bound = by / (PEAK_HBM_GBS * 1e9) > fl / (PEAK_MFMA_TFLOPS * 1e12)
+                out_rows.append({
+                    "P": P, "T": T, "bs": bs, "us": round(us, 2), "status": status,
+                    "TFLOPs": round(fl / (us * 1e-6) / 1e12, 1),
+                    "GBps": round(by / (us * 1e-6) / 1e9, 1),
+                    "flop_per_byte": round(fl / by, 1),
+                    "bound": "hbm" if hbm_bound else "mfma",
+                    "frac": round(f_hbm if hbm_bound else f_mfma, 4), "replays": reps})
+                log(f"sweep P={P} T={T} bs={bs}: {us:.1f} us, "
+                    f"{'hbm' if hbm_bound else 'mfma'} frac "
+                    f"{f_hbm if hbm_bound else f_mfma:.3f}")
+                va.close()
+                del q, pool, kvi, mask, out, lse, g
+                torch.cuda.empty_cache()
+    return out_rows
+
+
 def workload_names():
     import workloads
     return workloads.CONFIGS.keys()
@@ -235,6 +360,8 @@ def main():
                     help="also measure the fixed costs a single-launch (fused) merge would pay: "
                          "cooperative launch overhead and one grid barrier, against this step's "
                          "two-launch time (extra key single_launch_ab)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the step over P x T x bs (extra key sweep)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one elementwise kernel that reads and writes 256 MiB (for "
                          "scaling hardware byte counters)")
@@ -423,6 +550,8 @@ def main():
     }
     if single_launch is not None:
         result["single_launch_ab"] = single_launch
+    if args.sweep:
+        result["sweep"] = sweep()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w)
