@@ -338,6 +338,212 @@ def sweep(heads=64, budget_s=0.2, seed=0):
     return out_rows
 
 
+# ---- rocprofv3 summaries (profiles/*.txt), written from the csv output of these commands,
+# run from a scratch folder <out> on an MI355X (the profiler wants TMPDIR on a local disk):
+PROFILE_KERNELS = {
+    # file stem: (kernel-name fragment, sources whose sha256 the summary records)
+    "mfma_partial_kernel": ("mfma_partial_kernel<", ["verify_mfma.hip", "va_internal.h"]),
+    "simple_partial_kernel": ("simple_partial_kernel", ["verify_simple.hip", "va_internal.h"]),
+    "combine_kernel": ("combine_kernel<", ["verify_combine.hip", "va_internal.h"]),
+    "combine_rows_kernel": ("combine_rows_kernel<", ["verify_combine.hip", "va_internal.h"]),
+    "combine_few_rows_kernel": ("combine_few_rows_kernel", ["verify_combine.hip",
+                                                            "va_internal.h"]),
+    "build_mask_kernel": ("build_mask_kernel<", ["tree_ops.hip", "va_internal.h"]),
+    "accept_kernel": ("accept_kernel", ["tree_ops.hip", "va_internal.h"]),
+}
+PROFILE_BENCH_ARGS = "--steps 20 --warmup 5 --cold-steps 5 --no-cpu-baseline --copy-calibration"
+PROFILE_PASSES = (("trace", "--kernel-trace --stats"), ("fetch", "--pmc FETCH_SIZE"),
+                  ("write", "--pmc WRITE_SIZE"))
+WAVE_BENCH_ARGS = "--steps 10 --warmup 2 --cold-steps 2 --no-cpu-baseline"
+WAVE_PASSES = (
+    ("a", "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CU_CYCLES "
+          "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_ACTIVE_INST_VALU "
+          "SQ_WAVE_CYCLES SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE"),
+    ("b", "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_LDS SQ_INSTS_VALU "
+          "SQ_INSTS_MFMA SQ_WAIT_ANY SQ_ACTIVE_INST_MISC GRBM_GUI_ACTIVE"),
+    ("c", "SQ_LDS_IDX_ACTIVE SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_WAIT_INST_LDS "
+          "SQ_INST_LEVEL_LDS SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_LDS_ADDR_CONFLICT "
+          "SQ_INSTS_LDS_STORE_BANDWIDTH GRBM_GUI_ACTIVE"),
+)
+
+
+def profile_commands(workload):
+    """The commands whose output --summarize-profile reads (run in <out>, repository at <repo>)."""
+    cmds = ["cd <out> && export TMPDIR=/tmp"]
+    for sub, flags in PROFILE_PASSES:
+        cmds.append(f"rocprofv3 {flags} --output-format csv -d <out>/{sub} -o run -- python3 "
+                    f"<repo>/bench.py --workload {workload} {PROFILE_BENCH_ARGS} > "
+                    f"<out>/{sub}.json")
+    cmds.append(f"python3 <repo>/bench.py --workload {workload} --summarize-profile <out>")
+    return cmds
+
+
+def wave_commands(workload):
+    cmds = ["cd <out> && export TMPDIR=/tmp"]
+    for sub, counters in WAVE_PASSES:
+        cmds.append(f"rocprofv3 --pmc {counters} --output-format csv -d <out>/{sub} -o run -- "
+                    f"python3 <repo>/bench.py --workload {workload} {WAVE_BENCH_ARGS} > "
+                    f"<out>/{sub}.json")
+    cmds.append(f"python3 <repo>/bench.py --workload {workload} --summarize-wave-counters <out>")
+    return cmds
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(rows, counter, fragment):
+    """Counter summed over its instances for each dispatch of kernels matching `fragment`."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and fragment in r["Kernel_Name"]:
+            k = int(r["Dispatch_Id"])
+            per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def _sources_sha(sources):
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, "mla_tree_verify_paged_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def _bench_line(path):
+    lines = [ln for ln in open(path).read().splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1]) if lines else {}
+
+
+def summarize_profile(out_dir, workload):
+    """Writes profiles/<kernel>_<workload>.txt for every profiled kernel that ran: its kernel
+    trace and --stats row, and its HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the calibration kernel
+    (one fp32 elementwise multiply over 64 Mi elements: 256 MiB read, 256 MiB written)."""
+    import statistics
+    trace = _csv_rows(os.path.join(out_dir, "trace", "run_kernel_trace.csv"))
+    stats = _csv_rows(os.path.join(out_dir, "trace", "run_kernel_stats.csv"))
+    fetch = _csv_rows(os.path.join(out_dir, "fetch", "run_counter_collection.csv"))
+    write = _csv_rows(os.path.join(out_dir, "write", "run_counter_collection.csv"))
+    bench = _bench_line(os.path.join(out_dir, "trace.json"))
+
+    def calibration(rows, counter):
+        per = _per_dispatch(rows, counter, "MulFunctor")
+        return per[max(per)]  # the last elementwise multiply: the 256 MiB calibration kernel
+
+    cf, cw = calibration(fetch, "FETCH_SIZE"), calibration(write, "WRITE_SIZE")
+    ff = round(262144.0 / cf * 1000) / 1000
+    fw = round(262144.0 / cw * 1000) / 1000
+    written = []
+    for stem, (frag, sources) in PROFILE_KERNELS.items():
+        ks = [r for r in trace if frag in r["Kernel_Name"]]
+        if not ks:
+            continue
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in ks]
+        r0 = ks[-1]
+        names = sorted({r["Kernel_Name"].split("namespace)::")[-1].split("(va::")[0]
+                        for r in ks})
+        fpd = _per_dispatch(fetch, "FETCH_SIZE", frag)
+        wpd = _per_dispatch(write, "WRITE_SIZE", frag)
+        f_kib = statistics.mean(fpd.values())
+        w_kib = statistics.mean(wpd.values())
+        rd, wr = f_kib * ff * 1024, w_kib * fw * 1024
+        o = [f"# {stem} - workload '{workload}' (bench.py's '{workload}' configuration)", "",
+             "Commands (<repo> is the repository root, <out> a scratch folder):"]
+        o += ["  " + c for c in profile_commands(workload)]
+        o += ["", f"Kernel trace ({len(d)} dispatches: checked call, warm-up, timed steps, graph "
+                  "replays and cold replays):",
+              "  instantiations: " + ", ".join(names),
+              f"  average {statistics.mean(d):.3f} us, median {statistics.median(d):.3f} us, "
+              f"min {min(d):.3f} us, max {max(d):.3f} us",
+              f"  grid {r0['Grid_Size_X']} work-items, workgroup {r0['Workgroup_Size_X']}, LDS "
+              f"{r0['LDS_Block_Size']} B, VGPR {r0['VGPR_Count']}, AGPR "
+              f"{r0['Accum_VGPR_Count']}, SGPR {r0['SGPR_Count']}, scratch {r0['Scratch_Size']} B",
+              "", "rocprofv3 --stats (run_kernel_stats.csv):"]
+        for r in stats:
+            if frag in r["Name"]:
+                nm = r["Name"].split("namespace)::")[-1].split("(va::")[0]
+                o.append(f"  {nm}: calls {r['Calls']}, average {float(r['AverageNs']) / 1e3:.3f}"
+                         f" us, min {float(r['MinNs']) / 1e3:.3f} us, max "
+                         f"{float(r['MaxNs']) / 1e3:.3f} us, {r['Percentage']}% of kernel time")
+        o += ["", f"Byte counters (KiB per dispatch, mean over {len(fpd)} and {len(wpd)} "
+                  "dispatches):",
+              f"  FETCH_SIZE {f_kib:.1f}  x {ff:.3f} (calibration) = {rd / 2**20:.2f} MiB read",
+              f"  WRITE_SIZE {w_kib:.1f}  x {fw:.3f} (calibration) = {wr / 2**20:.2f} MiB written",
+              f"  calibration: the elementwise fp32 kernel that reads and writes 256 MiB reads "
+              f"FETCH_SIZE {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB", "",
+              f"  traffic per dispatch: {int(round(rd + wr))} bytes",
+              f"  kernel sources sha256 ({' + '.join(sources)}): {_sources_sha(sources)}"]
+        if bench:
+            o += ["", "bench.py line of the traced run (its own HIP-event timing, under the "
+                      "profiler):",
+                  f"  partial_kernel_us {bench.get('partial_kernel_us')}, combine_kernel_us "
+                  f"{bench.get('combine_kernel_us')}, value {bench.get('value')} us/step"]
+        path = os.path.join(ROOT, "profiles", f"{stem}_{workload}.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(o) + "\n")
+        written.append(path)
+    return written
+
+
+def summarize_wave_counters(out_dir, workload):
+    """Writes profiles/mfma_partial_kernel_<workload>_wave_counters.txt from the three SQ
+    counter passes: matrix-core busy time, issue and wait fractions, LDS traffic."""
+    import statistics
+    vals = {}
+    for sub, _ in WAVE_PASSES:
+        rows = _csv_rows(os.path.join(out_dir, sub, "run_counter_collection.csv"))
+        names = {r["Counter_Name"] for r in rows}
+        for c in names:
+            per = _per_dispatch(rows, c, "mfma_partial_kernel<")
+            if per:
+                vals[c] = (statistics.mean(per.values()), len(per))
+    simds = 256 * 4
+    v = {k: x[0] for k, x in vals.items()}
+    n = vals["SQ_WAVE_CYCLES"][1]
+    life = v["SQ_WAVE_CYCLES"] * 4 / simds          # SQ_WAVE_CYCLES counts 4-cycle units
+    busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+    co = v["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds
+    mops = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + v["SQ_INSTS_VALU_MFMA_MOPS_F16"]
+
+    def pct(counter):
+        return 100 * v[counter] * 4 / simds / life
+
+    srcs = PROFILE_KERNELS["mfma_partial_kernel"][1]
+    o = [f"# mfma_partial_kernel - workload '{workload}': wave-level counters", "",
+         "Commands (<repo> is the repository root, <out> a scratch folder):"]
+    o += ["  " + c for c in wave_commands(workload)]
+    o += ["", f"Raw counters (mean per dispatch over {n} dispatches; SQ_* summed over the chip):"]
+    o += [f"  {k:32s} {v[k]:.1f}" for k in sorted(v)]
+    o += ["", "Derived (1024 SIMDs, one wavefront per SIMD for the whole kernel; SQ_WAVE_CYCLES "
+              "and SQ_ACTIVE_*/SQ_WAIT_* count 4-cycle units, SQ_VALU_MFMA_* cycles):",
+          f"  matrix work: (MOPS_BF16 + MOPS_F16) x 512 = {mops * 512 / 1e9:.2f} GFLOP per "
+          "dispatch",
+          f"  wavefront lifetime: {life:.0f} cycles per SIMD",
+          f"  matrix core busy: {busy:.0f} cycles per SIMD = {100 * busy / life:.1f}% of the "
+          "lifetime",
+          f"  VALU issuing while the matrix core is busy: {co:.0f} cycles per SIMD "
+          f"({100 * co / busy:.1f}% of its busy time)",
+          f"  VALU issue {pct('SQ_ACTIVE_INST_VALU'):.1f}%, LDS issue "
+          f"{pct('SQ_ACTIVE_INST_LDS'):.1f}%, any issue {pct('SQ_ACTIVE_INST_ANY'):.1f}%, "
+          f"waiting on a dependency {pct('SQ_WAIT_INST_ANY'):.1f}% of the lifetime",
+          f"  instructions per wavefront: {v['SQ_INSTS_MFMA'] / simds:.0f} matrix, "
+          f"{v['SQ_INSTS_VALU'] / simds:.0f} VALU (matrix included), "
+          f"{v['SQ_INSTS_LDS'] / simds:.0f} LDS",
+          f"  LDS bank conflicts: {v['SQ_LDS_BANK_CONFLICT']:.0f} cycles",
+          f"  LDS bytes read by LDS instructions (64-byte units): "
+          f"{v['SQ_INSTS_LDS_LOAD_BANDWIDTH'] * 64 / 1e9:.2f} GB per dispatch, "
+          f"{v['SQ_INSTS_LDS_LOAD_BANDWIDTH'] * 64 / 256 / life:.0f} B per cycle per compute "
+          "unit over the lifetime (direct-to-LDS tile loads come on top)",
+          f"  waiting to issue an LDS instruction: {pct('SQ_WAIT_INST_LDS'):.1f}% of the lifetime",
+          "", f"  kernel sources sha256 ({' + '.join(srcs)}): {_sources_sha(srcs)}"]
+    path = os.path.join(ROOT, "profiles", f"mfma_partial_kernel_{workload}_wave_counters.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(o) + "\n")
+    return [path]
+
+
 def workload_names():
     import workloads
     return workloads.CONFIGS.keys()
@@ -365,7 +571,21 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one elementwise kernel that reads and writes 256 MiB (for "
                          "scaling hardware byte counters)")
+    ap.add_argument("--summarize-profile", metavar="OUT",
+                    help="write profiles/<kernel>_<workload>.txt from the rocprofv3 output in OUT "
+                         "(kernel trace with --stats, then FETCH_SIZE, then WRITE_SIZE); no GPU")
+    ap.add_argument("--summarize-wave-counters", metavar="OUT",
+                    help="write profiles/mfma_partial_kernel_<workload>_wave_counters.txt from "
+                         "the three SQ counter passes in OUT; no GPU")
     args = ap.parse_args()
+
+    if args.summarize_profile or args.summarize_wave_counters:
+        paths = (summarize_profile(args.summarize_profile, args.workload)
+                 if args.summarize_profile else
+                 summarize_wave_counters(args.summarize_wave_counters, args.workload))
+        for p in paths:
+            log(p)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

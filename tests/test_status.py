@@ -94,3 +94,20 @@ def test_non_positive_scale_is_rejected(kernel):
         with pytest.raises(B.VerifyAttnError) as e:
             run_gpu(w, kernel=kernel, dev=dev)
         assert e.value.status == B.VA_ERR_INVALID
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_mask_offset_near_int64_max_is_flagged(kernel):
+    """A corrupt mask_indptr entry next to INT64_MAX: the bounds check must not overflow, so
+    request 0 is rejected (rows empty, status flagged) and request 1 is untouched."""
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+    w = wl.build_workload("m64", np.random.default_rng(24), 8, [50, 70], [5, 6], 256)
+    dev = to_device(w)
+    dev["mask_indptr"][0] = 2**63 - 2
+    o, l, a, st = run_gpu(w, kernel=kernel, dev=dev)
+    assert st & B.VA_DEV_SEGMENT
+    first = 5 * 8
+    assert np.all(o[:first] == 0) and np.all(l[:first] == -np.inf) and np.all(a[:first] == -1)
+    ref = run_oracle(w)
+    rows = np.arange(first, w.num_tokens * w.num_heads)
+    compare(w, (o, l, a, 0), (ref[0][first:], ref[1][first:], ref[2][first:]), rows=rows)

@@ -154,3 +154,26 @@ def test_accept_matches_oracle(seed, max_path):
     assert np.array_equal(acc.cpu().numpy(), ra)
     assert np.array_equal(path.cpu().numpy(), rp)
     assert np.array_equal(nxt.cpu().numpy(), rn)
+
+
+def test_build_mask_offset_near_int64_max_is_flagged():
+    """A given mask_indptr entry next to INT64_MAX: the overflow-free bounds check rejects that
+    request (its rows unwritten, status flagged) and still writes the other one."""
+    rng = np.random.default_rng(71)
+    w = wl.build_workload("m64", rng, 2, [30, 40], [4, 5], 128)
+    indptr = w.mask_indptr.copy()
+    indptr[0] = 2**63 - 2
+    import torch
+    va = ctx_for(w)
+    parents = torch.from_numpy(np.concatenate(w.parents).astype(np.int64)).cuda()
+    size = int(w.mask_indptr[-1])
+    mask = torch.full((size,), 7, dtype=torch.uint8, device="cuda")
+    ind = torch.from_numpy(indptr).cuda()
+    va.build_mask(parents, torch.from_numpy(w.qo_indptr).cuda(),
+                  torch.from_numpy(w.kv_indptr).cuda(), mask, ind, write_mask_indptr=False)
+    torch.cuda.synchronize()
+    got = mask.cpu().numpy()
+    assert va.read_device_status() & 2
+    s1 = int(w.mask_indptr[1])
+    assert np.all(got[:s1] == 7)
+    assert np.array_equal(got[s1:], w.custom_mask[s1:])
