@@ -273,6 +273,100 @@ def test_row_tile_boundaries():
     compare(w, run_gpu(w, kernel="mfma", num_splits=3), ref)
 
 
+# ----------------------------------------------------------------------------- value ranges
+# Latent dims in four 128-dim groups at very different magnitudes: keys scaled by 2^6, 1,
+# 2^-6, 2^-12 per group and queries by the inverse powers of two, so every product q_d k_d, and
+# hence every score, is exactly that of the unscaled draw, while the values (the latent dims of
+# the keys) span 18 binary orders. The absolute 1e-2 bar cannot see an error in the small
+# groups, so each group is held to a bound relative to its own largest reference value:
+# 2^-8 covers the fp16 rounding of P (2^-11 of each weight) and of V, and the 16-bit partial
+# codes (one step = 2^-15 of the group's largest partial value) with room to spare; the
+# smallest group also absorbs fp16 subnormal rounding of V (at most 2^-25 absolute).
+GROUP_EXP = (6, 0, -6, -12)
+
+
+def _group_scaled(w):
+    import dataclasses
+    k = w.kv_rows_f32().copy()
+    q = w.q_f32().copy()
+    for g, e in enumerate(GROUP_EXP):
+        k[:, 128 * g:128 * (g + 1)] *= np.float32(2.0 ** e)
+        q[:, :, 128 * g:128 * (g + 1)] *= np.float32(2.0 ** -e)
+    return dataclasses.replace(w, name=w.name + "_groups", kv_rows=wl.to_bf16_bits(k),
+                               q=wl.to_bf16_bits(q))
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+@pytest.mark.parametrize("shape", ["rows1344", "rows24"])
+def test_value_groups_at_different_scales(kernel, shape):
+    rng = np.random.default_rng(77)
+    if shape == "rows1344":   # the 128-row path and the whole-row combine
+        base = wl.build_workload("groups", rng, 64, [3000, 700], [16, 5], 16384)
+    else:                     # the few-rows path and the quarter-row combine
+        base = wl.build_workload("groups", rng, 8, [5000], [3], 16384)
+    w = _group_scaled(base)
+    say(f"value groups {GROUP_EXP}, {shape}, {kernel}")
+    ref_o, ref_l, _ = run_oracle(w)
+    o, l, _, status = run_gpu(w, kernel=kernel)
+    assert status == 0
+    assert np.all(np.isfinite(o))
+    for g, e in enumerate(GROUP_EXP):
+        sl = slice(128 * g, 128 * (g + 1))
+        ref_max = float(np.max(np.abs(ref_o[:, sl])))
+        err = float(np.max(np.abs(o[:, sl] - ref_o[:, sl])))
+        say(f"  group {g} (x2^{e}): max|ref| {ref_max:.3e}, max err {err:.3e}")
+        assert err <= 2.0 ** -8 * ref_max + 2.0 ** -24, (g, err, ref_max)
+    # the scores did not change, so the lse matches the oracle's as in every other test
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(l), fin)
+
+
+# ----------------------------------------------------------------------------- argmax tie rule
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+@pytest.mark.parametrize("splits", [0, 8])
+def test_argmax_tie_across_splits_goes_to_the_lower_key(kernel, splits):
+    """One slot appears at key positions 300 and 2800 (in different key splits) and holds a
+    row aligned with every query, so both positions attain the maximum with bit-identical
+    scores: the argmax must be the lower position, 300 (the oracle's rule, pinned there by
+    brute force)."""
+    rng = np.random.default_rng(40)
+    h, p, t = 4, 3000, 2
+    w = wl.build_workload("tie", rng, h, [p], [t], 8192)
+    q = wl.bf16_bits_to_f32(w.q)
+    q[:, :, :] = q[0, 0]                       # every row has the same query
+    w.q = wl.to_bf16_bits(q)
+    rows = wl.bf16_bits_to_f32(w.kv_rows)
+    rows[300] = np.clip(q[0, 0] * 4.0, -30, 30)   # score ~ 4 |q|^2 scale: far above the rest
+    w.kv_rows = wl.to_bf16_bits(rows)
+    w.kv_indices[2800] = w.kv_indices[300]
+    w.kv_rows[2800] = w.kv_rows[300]
+    ref = run_oracle(w)
+    assert np.all(ref[2] == 300)
+    gpu = run_gpu(w, kernel=kernel, num_splits=splits)
+    assert np.all(gpu[2] == 300), np.unique(gpu[2])
+    compare(w, gpu, ref)
+
+
+# ----------------------------------------------------------------------------- split counts
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_split_counts_agree(kernel):
+    """One split, the device-chosen count and 256 splits: each run meets the oracle bar, and
+    the runs agree with each other within twice the per-run rounding scale (fp16 weights,
+    2^-11 of the largest value, and the 16-bit partial codes)."""
+    w = wl.build_workload("nsplit", np.random.default_rng(41), 64, [9000, 2500], [16, 8], 16384)
+    ref = run_oracle(w)
+    runs = {}
+    for s in (1, 0, 256):
+        runs[s] = run_gpu(w, kernel=kernel, num_splits=s)
+        compare(w, runs[s], ref)
+    vmax = float(np.abs(wl.bf16_bits_to_f32(w.kv_rows)[:, :512]).max())
+    tol = 2 * (2.0 ** -11 + 2.0 ** -15) * vmax
+    for s in (0, 256):
+        d = float(np.max(np.abs(runs[s][0] - runs[1][0])))
+        say(f"  splits {s} vs 1: max diff {d:.3e} (bound {tol:.3e})")
+        assert d <= tol
+
+
 # ----------------------------------------------------------------------------- value range
 @pytest.mark.parametrize("shape", ["rows1024", "rows24"])
 def test_latent_values_beyond_fp16_saturate_as_documented(shape):
