@@ -561,7 +561,8 @@ def main():
                     help="key slots: tree slots at the tail of each kv_indices segment, or "
                          "prefix-only kv_indices plus out_cache_loc")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=50)
+    ap.add_argument("--cold-steps", type=int, default=200,
+                    help="graph replays timed cold, each after a 512 MB flush (median, p10, p90)")
     ap.add_argument("--single-launch-ab", action="store_true",
                     help="also measure the fixed costs a single-launch (fused) merge would pay: "
                          "cooperative launch overhead and one grid barrier, against this step's "
@@ -667,7 +668,7 @@ def main():
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
         run_on(torch.cuda.current_stream().cuda_stream)
-    for _ in range(5):
+    for _ in range(20):  # warm-up replays
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
