@@ -98,6 +98,28 @@ double time_us(hipStream_t s, hipEvent_t e0, hipEvent_t e1, int reps, bool coop,
 
 }  // namespace
 
+namespace {
+
+// Owns the measurement's device resources, released on every return path.
+struct Resources {
+  uint32_t *bar = nullptr, *data = nullptr;
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipGraph_t g = nullptr;
+  hipGraphExec_t ge = nullptr;
+  ~Resources() {
+    if (ge) (void)hipGraphExecDestroy(ge);
+    if (g) (void)hipGraphDestroy(g);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (s) (void)hipStreamDestroy(s);
+    if (bar) (void)hipFree(bar);
+    if (data) (void)hipFree(data);
+  }
+};
+
+}  // namespace
+
 // Fills out[0..7]: plain launch (no barrier) us, cooperative launch (no barrier) us,
 // cooperative with one barrier pair us, cooperative with 33 barrier pairs us, graph replay of a
 // captured cooperative launch with one barrier pair us, barrier timeouts, visibility
@@ -107,45 +129,41 @@ extern "C" int single_launch_ab(double *out) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return int(e);
-  uint32_t *bar = nullptr, *data = nullptr;
-  hipStream_t s = nullptr;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  if ((e = hipMalloc(&bar, 4096)) != hipSuccess) return int(e);
-  if ((e = hipMalloc(&data, size_t(cus) * 128)) != hipSuccess) return int(e);
-  if ((e = hipMemset(bar, 0, 4096)) != hipSuccess) return int(e);
-  if ((e = hipStreamCreate(&s)) != hipSuccess) return int(e);
-  if ((e = hipEventCreate(&e0)) != hipSuccess) return int(e);
-  if ((e = hipEventCreate(&e1)) != hipSuccess) return int(e);
+  Resources r;
+  if ((e = hipMalloc(&r.bar, 4096)) != hipSuccess) return int(e);
+  if ((e = hipMalloc(&r.data, size_t(cus) * 128)) != hipSuccess) return int(e);
+  if ((e = hipMemset(r.bar, 0, 4096)) != hipSuccess) return int(e);
+  if ((e = hipStreamCreate(&r.s)) != hipSuccess) return int(e);
+  if ((e = hipEventCreate(&r.e0)) != hipSuccess) return int(e);
+  if ((e = hipEventCreate(&r.e1)) != hipSuccess) return int(e);
   const dim3 grid(static_cast<unsigned>(cus), 1, 1);
-  time_us(s, e0, e1, 3, true, grid, bar, data, 1, &e);  // warm-up
+  time_us(r.s, r.e0, r.e1, 3, true, grid, r.bar, r.data, 1, &e);  // warm-up
   if (e != hipSuccess) return int(e);
-  out[0] = time_us(s, e0, e1, 20, false, grid, bar, data, 0, &e);
-  if (e == hipSuccess) out[1] = time_us(s, e0, e1, 20, true, grid, bar, data, 0, &e);
-  if (e == hipSuccess) out[2] = time_us(s, e0, e1, 20, true, grid, bar, data, 1, &e);
-  if (e == hipSuccess) out[3] = time_us(s, e0, e1, 5, true, grid, bar, data, 33, &e);
+  out[0] = time_us(r.s, r.e0, r.e1, 20, false, grid, r.bar, r.data, 0, &e);
+  if (e == hipSuccess) out[1] = time_us(r.s, r.e0, r.e1, 20, true, grid, r.bar, r.data, 0, &e);
+  if (e == hipSuccess) out[2] = time_us(r.s, r.e0, r.e1, 20, true, grid, r.bar, r.data, 1, &e);
+  if (e == hipSuccess) out[3] = time_us(r.s, r.e0, r.e1, 5, true, grid, r.bar, r.data, 33, &e);
   if (e != hipSuccess) return int(e);
   // graph capture of the cooperative launch
   out[7] = 0.0;
   out[4] = -1.0;
-  hipGraph_t g = nullptr;
-  hipGraphExec_t ge = nullptr;
   int barriers = 1;
   uint32_t round = 99;
-  void *args[] = {&bar, &data, &barriers, &round};
-  if ((e = hipStreamBeginCapture(s, hipStreamCaptureModeGlobal)) != hipSuccess) return int(e);
+  void *args[] = {&r.bar, &r.data, &barriers, &round};
+  if ((e = hipStreamBeginCapture(r.s, hipStreamCaptureModeGlobal)) != hipSuccess) return int(e);
   const hipError_t ce =
-      hipLaunchCooperativeKernel((const void *)barrier_kernel, grid, dim3(256), args, 0, s);
-  e = hipStreamEndCapture(s, &g);
+      hipLaunchCooperativeKernel((const void *)barrier_kernel, grid, dim3(256), args, 0, r.s);
+  e = hipStreamEndCapture(r.s, &r.g);
   if (ce == hipSuccess && e == hipSuccess &&
-      hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) == hipSuccess) {
+      hipGraphInstantiate(&r.ge, r.g, nullptr, nullptr, 0) == hipSuccess) {
     bool ok = true;
-    for (int i = 0; i < 3 && ok; ++i) ok = hipGraphLaunch(ge, s) == hipSuccess;
-    ok = ok && hipStreamSynchronize(s) == hipSuccess;
-    if (ok && hipEventRecord(e0, s) == hipSuccess) {
-      for (int i = 0; i < 20 && ok; ++i) ok = hipGraphLaunch(ge, s) == hipSuccess;
+    for (int i = 0; i < 3 && ok; ++i) ok = hipGraphLaunch(r.ge, r.s) == hipSuccess;
+    ok = ok && hipStreamSynchronize(r.s) == hipSuccess;
+    if (ok && hipEventRecord(r.e0, r.s) == hipSuccess) {
+      for (int i = 0; i < 20 && ok; ++i) ok = hipGraphLaunch(r.ge, r.s) == hipSuccess;
       float ms = 0.f;
-      if (ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
-          hipEventElapsedTime(&ms, e0, e1) == hipSuccess) {
+      if (ok && hipEventRecord(r.e1, r.s) == hipSuccess && hipEventSynchronize(r.e1) == hipSuccess &&
+          hipEventElapsedTime(&ms, r.e0, r.e1) == hipSuccess) {
         out[4] = double(ms) * 1e3 / 20;
         out[7] = 1.0;
       }
@@ -154,15 +172,9 @@ extern "C" int single_launch_ab(double *out) {
     (void)hipGetLastError();
   }
   uint32_t h[4] = {0, 0, 0, 0};
-  if ((e = hipMemcpy(h, bar + 288, 16, hipMemcpyDeviceToHost)) != hipSuccess) return int(e);
+  if ((e = hipStreamSynchronize(r.s)) != hipSuccess) return int(e);
+  if ((e = hipMemcpy(h, r.bar + 288, 16, hipMemcpyDeviceToHost)) != hipSuccess) return int(e);
   out[5] = h[2];
   out[6] = h[3];
-  if (ge) (void)hipGraphExecDestroy(ge);
-  if (g) (void)hipGraphDestroy(g);
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
-  (void)hipStreamDestroy(s);
-  (void)hipFree(bar);
-  (void)hipFree(data);
   return 0;
 }
