@@ -590,8 +590,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the verify path is a single-GPU kernel library "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the verify path is a single-GPU kernel library; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
