@@ -1285,7 +1285,7 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
     __syncthreads();
     const uint32_t ok_t = g_okbits[b];
 
-    // this wavefront's partial scores of tile t (two chains) and the fp16 copy of the units
+    // this wavefront's partial scores of tile t (one chain) and the fp16 copy of the units
     // this thread loaded. Every LDS read of the phase is issued first: the assembly matrix
     // instructions end the compiler's scheduling regions, so reads placed between them would
     // each wait out a full LDS round trip.
@@ -1296,20 +1296,15 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i)
       craw[i] = *reinterpret_cast<const u32x4 *>(kraw + lo.cv_rd + kLatStride * i);
-    f32x16 sa, sb;
+    f32x16 part;
     static_for<0, kNarrowFrags>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       const bf16x8 av = __builtin_bit_cast(bf16x8, kf[i]);
       if constexpr (i == 0) {
         const f32x16 zero = {};
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], zero, 0, 0, 0);
-      } else if constexpr (i == 1) {
-        const f32x16 zero = {};
-        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], zero, 0, 0, 0);
-      } else if constexpr (i & 1) {
-        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], sb, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], zero, 0, 0, 0);
       } else {
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], sa, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[i], part, 0, 0, 0);
       }
       // the fp16 copy of one unit after each matrix instruction, so that the conversion
       // work issues while the matrix core runs
@@ -1320,9 +1315,6 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    f32x16 part;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) part[e] = sa[e] + sb[e];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       xbuf[(c.wave * 4 + q) * 64 + c.lane] =
