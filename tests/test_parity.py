@@ -133,6 +133,50 @@ def test_request_without_tree_tokens(kernel):
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_empty_batches_write_nothing(kernel):
+    """bs = 0, and a batch whose requests all have T_r = 0 (num_tokens = 0): the call succeeds,
+    enqueues nothing that writes, and leaves the output buffers as they were."""
+    import torch
+    from mla_tree_verify_paged_amd import VerifyAttn
+    from mla_tree_verify_paged_amd.device_inputs import to_device
+    rng = np.random.default_rng(11)
+    w = wl.build_workload("t0all", rng, 8, [40, 0, 25], [0, 0, 0], 128)
+    assert w.num_tokens == 0
+    dev = to_device(w)
+    va = VerifyAttn(8, max_batch=4, max_q_per_req=4, max_q_tokens=8, kernel=kernel)
+    q = torch.zeros((8, 8, 576), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((8, 8, 512), 3.0, device="cuda")
+    lse = torch.full((8, 8), 5.0, device="cuda")
+    am = torch.full((8, 8), 7, dtype=torch.int32, device="cuda")
+    for bs in (0, w.bs):
+        va.run(q, dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"], dev["qo_indptr"],
+               dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, am, bs=bs,
+               num_tokens=0)
+        torch.cuda.synchronize()
+        assert va.read_device_status() == 0
+        assert bool((out == 3.0).all()) and bool((lse == 5.0).all()) and bool((am == 7).all())
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_many_heads(kernel):
+    """H = 128: a 128-row tile is one token's heads; 5 tokens give 5 row tiles."""
+    rng = np.random.default_rng(12)
+    w = wl.build_workload("h128", rng, 128, [900], [5], 4096)
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_large_tree(kernel):
+    """A 384-node draft tree at H = 8 (3072 rows: the wavefront-per-row combine) over a short
+    prefix, so most keys of most rows are tree keys under the mask."""
+    rng = np.random.default_rng(13)
+    w = wl.build_workload("bigtree", rng, 8, [200], [384], 4096)
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel), ref)
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
 @pytest.mark.parametrize("shape", ["short", "rows2560", "rows48"])
 def test_bf16_output(kernel, shape):
     """bf16 output in each combine launch shape: 1024 rows (a workgroup per row), 2560 rows
