@@ -177,3 +177,38 @@ def test_build_mask_offset_near_int64_max_is_flagged():
     s1 = int(w.mask_indptr[1])
     assert np.all(got[:s1] == 7)
     assert np.array_equal(got[s1:], w.custom_mask[s1:])
+
+
+def test_tree_kernels_at_the_node_limit():
+    """A 2048-node tree (the largest max_q_per_req the tree kernels take) next to a 1-node one:
+    the mask byte-exact against the tree oracle, and acceptance along a 2047-step chain whose
+    draft tokens all match (one wavefront walks the whole path)."""
+    import torch
+    from mla_tree_verify_paged_amd import VerifyAttn
+    rng = np.random.default_rng(72)
+    w = wl.build_workload("t2048", rng, 1, [100, 50], [2048, 1], 4096)
+    parents = np.concatenate(w.parents)
+    ref_mask, ref_ind = to.build_mask(parents, w.qo_indptr, w.kv_indptr)
+    mask, ind, status = gpu_mask(w, False)
+    assert status == 0
+    assert np.array_equal(ind, ref_ind) and np.array_equal(mask, ref_mask)
+
+    t = 2048
+    chain = np.arange(-1, t - 1, dtype=np.int64)        # node k's parent is k - 1
+    draft = rng.integers(0, 1000, t).astype(np.int64)
+    target = np.roll(draft, -1)                          # node k's target is node k+1's draft
+    target[-1] = 5
+    qo = np.array([0, t], np.int64)
+    va = VerifyAttn(8, max_batch=1, max_q_per_req=t, max_q_tokens=t)
+    acc = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+    path = torch.full((1, t), -9, dtype=torch.int64, device="cuda")
+    nxt = torch.full((1,), -9, dtype=torch.int64, device="cuda")
+    d = lambda a: torch.from_numpy(a).cuda()
+    va.accept(d(chain), d(draft), d(target), d(qo), acc, path, nxt, num_tokens=t)
+    torch.cuda.synchronize()
+    ra, rp, rn = to.accept(chain, draft, target, qo, t)
+    assert va.read_device_status() == 0
+    assert int(ra[0]) == t - 1
+    assert np.array_equal(acc.cpu().numpy(), ra)
+    assert np.array_equal(path.cpu().numpy(), rp)
+    assert np.array_equal(nxt.cpu().numpy(), rn)
