@@ -416,7 +416,7 @@ def _bench_line(path):
     return json.loads(lines[-1]) if lines else {}
 
 
-def summarize_profile(out_dir, workload):
+def summarize_profile(out_dir, workload, dest=None):
     """Writes profiles/<kernel>_<workload>.txt for every profiled kernel that ran: its kernel
     trace and --stats row, and its HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled by what the same counter reads for the calibration kernel
@@ -480,14 +480,14 @@ def summarize_profile(out_dir, workload):
                       "profiler):",
                   f"  partial_kernel_us {bench.get('partial_kernel_us')}, combine_kernel_us "
                   f"{bench.get('combine_kernel_us')}, value {bench.get('value')} us/step"]
-        path = os.path.join(ROOT, "profiles", f"{stem}_{workload}.txt")
+        path = os.path.join(dest or os.path.join(ROOT, "profiles"), f"{stem}_{workload}.txt")
         with open(path, "w") as f:
             f.write("\n".join(o) + "\n")
         written.append(path)
     return written
 
 
-def summarize_wave_counters(out_dir, workload):
+def summarize_wave_counters(out_dir, workload, dest=None):
     """Writes profiles/mfma_partial_kernel_<workload>_wave_counters.txt from the three SQ
     counter passes: matrix-core busy time, issue and wait fractions, LDS traffic."""
     import statistics
@@ -538,7 +538,8 @@ def summarize_wave_counters(out_dir, workload):
           "unit over the lifetime (direct-to-LDS tile loads come on top)",
           f"  waiting to issue an LDS instruction: {pct('SQ_WAIT_INST_LDS'):.1f}% of the lifetime",
           "", f"  kernel sources sha256 ({' + '.join(srcs)}): {_sources_sha(srcs)}"]
-    path = os.path.join(ROOT, "profiles", f"mfma_partial_kernel_{workload}_wave_counters.txt")
+    path = os.path.join(dest or os.path.join(ROOT, "profiles"),
+                        f"mfma_partial_kernel_{workload}_wave_counters.txt")
     with open(path, "w") as f:
         f.write("\n".join(o) + "\n")
     return [path]
