@@ -26,10 +26,11 @@
 //    ds_read_b64_tr_b16. The P fragment is the S accumulator itself: key slots are permuted
 //    the same way in both operands;
 //  * the tile loop is software-pipelined: the P.V products of tile t are interleaved with the
-//    QK^T products of tile t+1 (so consecutive matrix instructions are independent), with the
-//    fp16 conversion of tile t+1 and the loads of tile t+2 slotted between them. With one
-//    wavefront per SIMD (the 256 output accumulators per lane rule out more) every issued
-//    instruction costs issue time, so the loop is written to issue as few as possible;
+//    QK^T products of tile t+1 (so the scores of tile t+1 are ready when tile t's products
+//    end), with the fp16 conversion of tile t+1 and the loads of tile t+2 slotted between
+//    them. With one wavefront per SIMD (the 256 output accumulators per lane rule out more)
+//    the other instructions issue between the matrix instructions rather than beside them, so
+//    the loop is written to issue as few as possible;
 //  * the running max is rescaled lazily (only when it grows by more than 2^8), in place in
 //    the accumulation registers, so the 256 fp32 accumulators per lane never leave them;
 //  * workgroups are mapped so that all row tiles of one key split run on the same XCD and
