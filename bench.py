@@ -243,6 +243,34 @@ def single_launch_ab(partial_us, combine_us, step_us):
     }
 
 
+def lds_probe():
+    """How fast LDS feeds the matrix cores at one and two wavefronts per SIMD, per operand read
+    form, and what a dependent accumulation chain costs (csrc/lds_mfma_probe.hip)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "mla_tree_verify_paged_amd", "liblds_mfma_probe.so"))
+    lib.lds_mfma_probe.argtypes = [ctypes.POINTER(ctypes.c_double)]
+    lib.lds_mfma_probe.restype = ctypes.c_int
+    out = (ctypes.c_double * 20)()
+    rc = lib.lds_mfma_probe(out)
+    if rc != 0:
+        return {"error": f"hip error {rc}"}
+    forms = ["b128 (K fragment)", "two tr_b64 (V^T fragment)", "alternating",
+             "b128 + two tr_b64 (2 KB per product)"]
+    feed = {}
+    for w in range(2):
+        for f, name in enumerate(forms):
+            feed.setdefault(name, {})[f"{w + 1} wave/SIMD"] = {
+                "mfma_util_pct": round(out[8 * w + 2 * f], 1),
+                "lds_bytes_per_clk_per_cu": round(out[8 * w + 2 * f + 1], 1)}
+    return {"feed": feed,
+            "cycles_per_32x32x16_product": {"1 chain": round(out[16], 2),
+                                            "2 chains": round(out[17], 2),
+                                            "4 chains": round(out[18], 2)},
+            "clock_ghz": round(out[19], 2),
+            "method": "one 256- or 512-thread workgroup per CU (96 KB LDS), each product's 1 KB "
+                      "operand read 4 products ahead; utilisation = matrix cycles / elapsed "
+                      "cycles"}
+
+
 SWEEP_P = (1024, 5700, 23000, 65536, 131072)
 SWEEP_T = (1, 4, 16, 64)
 SWEEP_BS = (1, 8, 32)
@@ -568,6 +596,9 @@ def main():
                     help="also measure the fixed costs a single-launch (fused) merge would pay: "
                          "cooperative launch overhead and one grid barrier, against this step's "
                          "two-launch time (extra key single_launch_ab)")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="also measure how fast LDS feeds the matrix cores at one and two "
+                         "wavefronts per SIMD (extra key lds_probe)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the step over P x T x bs (extra key sweep)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -774,6 +805,9 @@ def main():
         result["single_launch_ab"] = single_launch
     if args.sweep:
         result["sweep"] = sweep()
+    if args.lds_probe:
+        result["lds_probe"] = lds_probe()
+        log(f"lds probe: {result['lds_probe']}")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(w)

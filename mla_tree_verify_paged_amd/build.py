@@ -36,15 +36,28 @@ AB_SOURCE = "single_launch_ab.hip"  # a separate measurement library, not the ve
 AB_LIB = os.path.join(HERE, "libsingle_launch_ab.so")
 
 
-def build_ab(verbose: bool = False) -> str:
-    """Builds the single-launch A/B measurement library (bench.py --single-launch-ab)."""
-    tmp = AB_LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, AB_SOURCE), "-o", tmp]
+PROBE_SOURCE = "lds_mfma_probe.hip"  # a separate measurement library
+PROBE_LIB = os.path.join(HERE, "liblds_mfma_probe.so")
+
+
+def _build_one(source: str, lib: str) -> str:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, source), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-8000:]}")
-    os.replace(tmp, AB_LIB)
-    return AB_LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build_ab(verbose: bool = False) -> str:
+    """Builds the single-launch A/B measurement library (bench.py --single-launch-ab)."""
+    return _build_one(AB_SOURCE, AB_LIB)
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Builds the LDS/matrix-core probe library (bench.py --lds-probe)."""
+    return _build_one(PROBE_SOURCE, PROBE_LIB)
 
 
 def build(verbose: bool = False, extra=()) -> str:
@@ -65,3 +78,4 @@ def build(verbose: bool = False, extra=()) -> str:
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_ab())
+    print(build_probe())
