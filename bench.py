@@ -371,6 +371,7 @@ def sweep(heads=64, budget_s=0.2, seed=0):
 PROFILE_KERNELS = {
     # file stem: (kernel-name fragment, sources whose sha256 the summary records)
     "mfma_partial_kernel": ("mfma_partial_kernel<", ["verify_mfma.hip", "va_internal.h"]),
+    "mfma_partial_ws_kernel": ("mfma_partial_ws_kernel<", ["verify_mfma.hip", "va_internal.h"]),
     "simple_partial_kernel": ("simple_partial_kernel", ["verify_simple.hip", "va_internal.h"]),
     "combine_kernel": ("combine_kernel<", ["verify_combine.hip", "va_internal.h"]),
     "combine_rows_kernel": ("combine_rows_kernel<", ["verify_combine.hip", "va_internal.h"]),
@@ -516,36 +517,44 @@ def summarize_profile(out_dir, workload, dest=None):
 
 
 def summarize_wave_counters(out_dir, workload, dest=None):
-    """Writes profiles/mfma_partial_kernel_<workload>_wave_counters.txt from the three SQ
-    counter passes: matrix-core busy time, issue and wait fractions, LDS traffic."""
+    """Writes profiles/<partial kernel>_<workload>_wave_counters.txt from the three SQ counter
+    passes: matrix-core busy time, issue and wait fractions, LDS traffic. The partial kernel is
+    the 8-wavefront variant when it ran, else the 4-wavefront one."""
     import statistics
+    rows_by = {sub: _csv_rows(os.path.join(out_dir, sub, "run_counter_collection.csv"))
+               for sub, _ in WAVE_PASSES}
+    ws = any("mfma_partial_ws_kernel<" in r["Kernel_Name"] for r in rows_by[WAVE_PASSES[0][0]])
+    stem = "mfma_partial_ws_kernel" if ws else "mfma_partial_kernel"
+    waves_per_simd = 2 if ws else 1
     vals = {}
     for sub, _ in WAVE_PASSES:
-        rows = _csv_rows(os.path.join(out_dir, sub, "run_counter_collection.csv"))
+        rows = rows_by[sub]
         names = {r["Counter_Name"] for r in rows}
         for c in names:
-            per = _per_dispatch(rows, c, "mfma_partial_kernel<")
+            per = _per_dispatch(rows, c, stem + "<")
             if per:
                 vals[c] = (statistics.mean(per.values()), len(per))
     simds = 256 * 4
     v = {k: x[0] for k, x in vals.items()}
     n = vals["SQ_WAVE_CYCLES"][1]
-    life = v["SQ_WAVE_CYCLES"] * 4 / simds          # SQ_WAVE_CYCLES counts 4-cycle units
+    # SQ_WAVE_CYCLES counts 4-cycle units and sums over the wavefronts a SIMD holds
+    life = v["SQ_WAVE_CYCLES"] * 4 / simds / waves_per_simd
     busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
     co = v["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds
     mops = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + v["SQ_INSTS_VALU_MFMA_MOPS_F16"]
 
-    def pct(counter):
+    def pct(counter):  # per SIMD (both wavefronts together when there are two)
         return 100 * v[counter] * 4 / simds / life
 
-    srcs = PROFILE_KERNELS["mfma_partial_kernel"][1]
-    o = [f"# mfma_partial_kernel - workload '{workload}': wave-level counters", "",
+    srcs = PROFILE_KERNELS[stem][1]
+    o = [f"# {stem} - workload '{workload}': wave-level counters", "",
          "Commands (<repo> is the repository root, <out> a scratch folder):"]
     o += ["  " + c for c in wave_commands(workload)]
     o += ["", f"Raw counters (mean per dispatch over {n} dispatches; SQ_* summed over the chip):"]
     o += [f"  {k:32s} {v[k]:.1f}" for k in sorted(v)]
-    o += ["", "Derived (1024 SIMDs, one wavefront per SIMD for the whole kernel; SQ_WAVE_CYCLES "
-              "and SQ_ACTIVE_*/SQ_WAIT_* count 4-cycle units, SQ_VALU_MFMA_* cycles):",
+    o += ["", f"Derived (1024 SIMDs, {waves_per_simd} wavefront(s) per SIMD for the whole "
+              "kernel; SQ_WAVE_CYCLES and SQ_ACTIVE_*/SQ_WAIT_* count 4-cycle units summed over "
+              "wavefronts, SQ_VALU_MFMA_* cycles; issue and wait fractions are per SIMD):",
           f"  matrix work: (MOPS_BF16 + MOPS_F16) x 512 = {mops * 512 / 1e9:.2f} GFLOP per "
           "dispatch",
           f"  wavefront lifetime: {life:.0f} cycles per SIMD",
@@ -556,7 +565,7 @@ def summarize_wave_counters(out_dir, workload, dest=None):
           f"  VALU issue {pct('SQ_ACTIVE_INST_VALU'):.1f}%, LDS issue "
           f"{pct('SQ_ACTIVE_INST_LDS'):.1f}%, any issue {pct('SQ_ACTIVE_INST_ANY'):.1f}%, "
           f"waiting on a dependency {pct('SQ_WAIT_INST_ANY'):.1f}% of the lifetime",
-          f"  instructions per wavefront: {v['SQ_INSTS_MFMA'] / simds:.0f} matrix, "
+          f"  instructions per SIMD: {v['SQ_INSTS_MFMA'] / simds:.0f} matrix, "
           f"{v['SQ_INSTS_VALU'] / simds:.0f} VALU (matrix included), "
           f"{v['SQ_INSTS_LDS'] / simds:.0f} LDS",
           f"  LDS bank conflicts: {v['SQ_LDS_BANK_CONFLICT']:.0f} cycles",
@@ -567,7 +576,7 @@ def summarize_wave_counters(out_dir, workload, dest=None):
           f"  waiting to issue an LDS instruction: {pct('SQ_WAIT_INST_LDS'):.1f}% of the lifetime",
           "", f"  kernel sources sha256 ({' + '.join(srcs)}): {_sources_sha(srcs)}"]
     path = os.path.join(dest or os.path.join(ROOT, "profiles"),
-                        f"mfma_partial_kernel_{workload}_wave_counters.txt")
+                        f"{stem}_{workload}_wave_counters.txt")
     with open(path, "w") as f:
         f.write("\n".join(o) + "\n")
     return [path]
@@ -608,7 +617,7 @@ def main():
                     help="write profiles/<kernel>_<workload>.txt from the rocprofv3 output in OUT "
                          "(kernel trace with --stats, then FETCH_SIZE, then WRITE_SIZE); no GPU")
     ap.add_argument("--summarize-wave-counters", metavar="OUT",
-                    help="write profiles/mfma_partial_kernel_<workload>_wave_counters.txt from "
+                    help="write profiles/<partial kernel>_<workload>_wave_counters.txt from "
                          "the three SQ counter passes in OUT; no GPU")
     args = ap.parse_args()
 
@@ -641,7 +650,10 @@ def main():
                     num_splits=args.splits, kernel=args.kernel)
     info = va.info
     kernel_name = {1: "simple", 2: "mfma"}[info.kernel]
-    log(f"kernel={kernel_name} splits={info.num_splits} workspace={info.workspace_bytes}")
+    # the MFMA partial kernel's variant: 8 wavefronts per workgroup (two per SIMD) or 4
+    part_stem = "mfma_partial_ws_kernel" if info.partial_waves == 8 else "mfma_partial_kernel"
+    log(f"kernel={kernel_name} splits={info.num_splits} workspace={info.workspace_bytes} "
+        f"partial waves={info.partial_waves}")
     out = torch.empty((w.num_tokens, w.num_heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.num_tokens, w.num_heads), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -743,7 +755,7 @@ def main():
     log(f"tree ops: {tree_ops}")
 
     by, fl = algorithmic_work(w)
-    traffic = (counter_traffic("mfma_partial_kernel", w.name, ["verify_mfma.hip", "va_internal.h"])
+    traffic = (counter_traffic(part_stem, w.name, ["verify_mfma.hip", "va_internal.h"])
                if kernel_name == "mfma" else None)
     part_s = part_ms.mean() * 1e-3
     us = ms_per_step * 1e3
@@ -796,7 +808,8 @@ def main():
             "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": f"{kernel_name} partial (split-K)",
+            "kernel": (f"{part_stem} (split-K partial)" if kernel_name == "mfma"
+                       else "simple_partial_kernel (split-K partial)"),
         },
         "tree_ops": tree_ops,
         "cpu_baseline": None,

@@ -145,6 +145,11 @@ typedef struct {
   int32_t rows_per_block; /* (token, head) rows handled by one partial workgroup           */
   int32_t row_tiles_per_req; /* row tiles a request can have (ceil(max_q_per_req*H / rows)) */
   size_t workspace_bytes; /* bytes of workspace in use                                     */
+  int32_t partial_waves;  /* wavefronts per partial workgroup: 8 (two per SIMD: four hold the
+                             query rows and compute scores and softmax, four hold most of the
+                             output accumulators and stage the key tiles) for the MFMA kernel
+                             when num_heads is a multiple of 64 (no work item then has 32
+                             rows or fewer), else 4                                         */
 } verify_attn_info;
 
 /* Workspace bytes a config needs (0 if the config is invalid): per partial row about 1052

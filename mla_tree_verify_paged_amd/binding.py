@@ -44,7 +44,7 @@ class verify_attn_info(ctypes.Structure):
     _fields_ = [
         ("kernel", ctypes.c_int32), ("num_splits", ctypes.c_int32),
         ("rows_per_block", ctypes.c_int32), ("row_tiles_per_req", ctypes.c_int32),
-        ("workspace_bytes", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t), ("partial_waves", ctypes.c_int32),
     ]
 
 

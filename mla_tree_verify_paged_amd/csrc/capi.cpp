@@ -439,6 +439,8 @@ va_status verify_attn_get_info(const verify_attn_ctx *ctx, verify_attn_info *inf
   info->rows_per_block = ctx->d.rows_per_block;
   info->row_tiles_per_req = ctx->d.row_tiles;
   info->workspace_bytes = ctx->d.bytes;
+  info->partial_waves =
+      ctx->d.kernel == VA_KERNEL_MFMA ? va::mfma_partial_waves(ctx->cfg.num_heads) : 4;
   return ok();
 }
 

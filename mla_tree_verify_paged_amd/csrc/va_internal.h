@@ -198,5 +198,9 @@ hipError_t launch_accept(const AcceptArgs &a, hipStream_t st);
 // Rows per workgroup of each partial kernel (fixes the grid).
 constexpr int kSimpleHeadsPerBlock = 4;
 constexpr int kMfmaRowsPerBlock = 128;
+// Wavefronts of an MFMA partial workgroup: with H a multiple of 64 a row tile holds 64 or 128
+// rows, never 32 or fewer, and the 8-wavefront (two per SIMD) variant runs; otherwise the
+// 4-wavefront one, which also has the path for items of at most 32 rows.
+constexpr int mfma_partial_waves(int num_heads) { return num_heads % 64 == 0 ? 8 : 4; }
 
 }  // namespace va

@@ -557,7 +557,9 @@ __device__ __forceinline__ void step(const Ctx &c, const LaneOffs &lo, const Ste
 }
 
 // ---- the rest of the softmax of one tile's scores: mask, max (and argmax), lazy rescale
-template <bool kArgmax, int kOBlocks = kDBlocks>
+// (kAgpr: the output accumulators sit in AGPRs, out of the compiler's sight; kLean: read the
+// mask bytes of a tail tile four at a time, in a loop, to keep registers free)
+template <bool kArgmax, int kOBlocks = kDBlocks, bool kAgpr = true, bool kLean = false>
 __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits, f32x16 &sacc,
                                           f32x16 *o, RowState &st, float c2, bool row_ok,
                                           const uint8_t *mseg, uint32_t moff) {
@@ -570,7 +572,20 @@ __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits,
     const int jh = kb + 4 * c.half;
     const uint32_t okh = okbits >> (4 * c.half);
     uint32_t tree_vis = 0xffffffffu;
-    if (tail) {
+    if (tail && kLean) {
+      tree_vis = 0;
+#pragma unroll 1
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b4 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = jh + 8 * q + i;
+          const uint8_t mv = mseg[moff + uint32_t(min(j, c.k1 - 1))];
+          b4 |= uint32_t(j < c.P || (row_ok && mv != 0)) << i;
+        }
+        tree_vis |= b4 << (4 * q);
+      }
+    } else if (tail) {
       // the lane's row's mask bytes (addresses clamped into the row; keys past the split
       // are already unusable in okbits)
       uint8_t mb[16];
@@ -625,10 +640,17 @@ __device__ __forceinline__ void score_max(const Ctx &c, int kb, uint32_t okbits,
   if (__any(rescale)) {
     const float alpha = rescale ? __builtin_amdgcn_exp2f(st.m - tmax) : 1.f;
     st.lsum *= alpha;
-    matrix_drain();
+    if constexpr (kAgpr) {
+      matrix_drain();
 #pragma unroll
-    for (int d = 0; d < kOBlocks; ++d) scale_acc(o[d], alpha);
-    matrix_drain();
+      for (int d = 0; d < kOBlocks; ++d) scale_acc(o[d], alpha);
+      matrix_drain();
+    } else {
+#pragma unroll
+      for (int d = 0; d < kOBlocks; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+    }
   }
   if (need) st.m = tmax;
 }
@@ -1443,6 +1465,562 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
   }
 }
 
+// ---- two wavefronts per SIMD: score and value wavefronts
+//
+// A variant of the 128-row item for H a multiple of 64 (then no item has 32 rows or fewer).
+// One wavefront per SIMD leaves nothing to issue beside a wavefront's matrix instructions;
+// this one runs eight, two per SIMD, each within 256 registers:
+//  * score wavefront g (g < 4) holds the 32 query rows of row group g (144 registers) and
+//    computes S^T = K Q^T of every tile, the mask, max, argmax and lazy rescale, and the
+//    fp16 P, which it hands to its value wavefront through LDS; it accumulates output dims
+//    [0, 128) (4 of the 16 dim blocks, 64 registers);
+//  * value wavefront 4 + g accumulates dims [128, 512) of the same rows (12 blocks, 192
+//    registers) from that P, and does all the staging the four wavefronts of the other
+//    variant share (slots, tile loads, fp16 copy), as staging wavefront g.
+// Both kinds take the same barriers: one per tile as before, so P(t) is written in step t-1
+// and read in step t from a buffer of its own parity. The value wavefront mirrors the running
+// max: it receives it with P and rescales its accumulators exactly when the score wavefront
+// rescales its own (same operands, same instruction).
+constexpr int kWsThreads = 2 * kThreads;
+constexpr int kABlocks = 4;                   // output dim blocks of a score wavefront
+constexpr int kBBlocks = kDBlocks - kABlocks;   // 12 of a value wavefront
+constexpr int kSplitG = kABlocks / 4;           // the scale group the two kinds may share
+constexpr bool kSplit = kABlocks % 4 != 0;      // whether they share it
+constexpr int kDepthA = 2;                      // operand reads in flight, score wavefront
+constexpr int kDepthB = 3;                      // and value wavefront
+constexpr int kXPair = 2 * 64 * 16 + 64 * 4;  // P (two 16-key chunks) and the running max
+constexpr int kWsXOff = kLdsBytes;
+constexpr int kWsLds = kWsXOff + 2 * kWaves * kXPair;  // 162,816
+static_assert(kWsLds + sizeof(g_slots) + sizeof(g_okbits) <= 160 * 1024, "LDS budget");
+static_assert(kVOff + kWaves * 32 * 16 * (kQFrags + 1) <= kWsLds, "query halves fit in LDS");
+__shared__ __attribute__((aligned(16))) char g_ldsw[kWsLds];
+
+// The operand fragment of a QK^T fragment (kPv false, kIdx 0..35) or of P.V product kIdx
+// (key chunk kIdx / kNBlk, dim block kBlk0 + kIdx % kNBlk).
+template <bool kPv, int kIdx, int kBlk0, int kNBlk>
+__device__ __forceinline__ u32x4 op_frag(const char *klat, const char *krope, const char *vtr) {
+  u32x4 r;
+  if constexpr (!kPv) {
+    if constexpr (kIdx < kLatFrags)
+      r = *reinterpret_cast<const u32x4 *>(klat + 32 * kIdx);
+    else
+      r = *reinterpret_cast<const u32x4 *>(krope + 256 * (kIdx - kLatFrags));
+  } else {
+    constexpr int ch = kIdx / kNBlk, d = kBlk0 + kIdx % kNBlk;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const fp16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+          (lds_fp16x4 *)(vtr + (16 * ch + 8 * rr) * kVRow + 64 * d));
+      const u32x2 w = __builtin_bit_cast(u32x2, x);
+      r[2 * rr] = w[0];
+      r[2 * rr + 1] = w[1];
+    }
+  }
+  return r;
+}
+
+// Score wavefront, one step: kFirst - QK^T of tile 0; kMain - P(t).V(t) of its dim blocks,
+// then QK^T of tile t+1 (P(t) is dead before the score accumulators are live); kLast -
+// P(t).V(t).
+template <int K>
+__device__ __forceinline__ void ws_score_step(const LaneOffs &lo, const char *kraw,
+                                              const char *vrd, const bf16x8 *qf, f32x16 *o,
+                                              const f16x8 *pf, f32x16 &sa) {
+  constexpr int kPV = K == kFirst ? 0 : 2 * kABlocks;
+  constexpr int kQK = K == kLast ? 0 : kQFrags;
+  constexpr int N = kPV + kQK;
+  constexpr OpTable<N> T = [] {
+    OpTable<N> t{};
+    int p = 0;
+    for (int i = 0; i < kPV; ++i) t.op[p++] = Op{1, int8_t(i)};
+    for (int i = 0; i < kQK; ++i) t.op[p++] = Op{0, int8_t(i)};
+    return t;
+  }();
+  const char *klat = kraw + lo.k_lat;
+  const char *krope = kraw + lo.k_rope;
+  const char *vtr = vrd + lo.v_tr;
+  u32x4 fr[kDepthA + 1];
+  auto load = [&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    if constexpr (p < N) {
+      constexpr Op op = T.op[p];
+      fr[p % (kDepthA + 1)] = op_frag<op.pv != 0, op.idx, 0, kABlocks>(klat, krope, vtr);
+    }
+  };
+  static_for<0, kDepthA>(load);
+  static_for<0, N>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    constexpr Op op = T.op[p];
+    load(std::integral_constant<int, p + kDepthA>{});
+    const u32x4 a = fr[p % (kDepthA + 1)];
+    if constexpr (op.pv) {
+      constexpr int ch = op.idx / kABlocks, d = op.idx % kABlocks;
+      o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), pf[ch], o[d],
+                                                    0, 0, 0);
+    } else {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+      if constexpr (op.idx == 0) {
+        const f32x16 zero = {};
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[0], zero, 0, 0, 0);
+      } else {
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[op.idx], sa, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// Value wavefront: takes P(t) and the max it was computed against.
+__device__ __forceinline__ float ws_take(const char *x, int lane, f16x8 *pf) {
+  pf[0] = *reinterpret_cast<const f16x8 *>(x + 16 * lane);
+  pf[1] = *reinterpret_cast<const f16x8 *>(x + 1024 + 16 * lane);
+  return *reinterpret_cast<const float *>(x + 2048 + 4 * lane);
+}
+// ... and rescales its accumulators when the max moved (mb: the max they are relative to).
+__device__ __forceinline__ void ws_rescale(float mn, float &mb, f32x16 *o) {
+  const bool rescale = mn != mb && mb != -INFINITY;
+  if (__any(rescale)) {
+    const float alpha = rescale ? __builtin_amdgcn_exp2f(mb - mn) : 1.f;
+#pragma unroll
+    for (int d = 0; d < kBBlocks; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+  }
+  mb = mn;
+}
+
+// Value wavefront, one step. With K == kMain it first stages (loads of tile t+2, the slots of
+// tile t+3, the fp16 copy of tile t+1), while the score wavefront's QK^T chain holds the
+// matrix core: issue is in order, so staging placed after a product would wait for that
+// chain too. Then P(t).V(t) of its dim blocks, which runs while the score wavefront does the
+// softmax of tile t+1.
+template <int K>
+__device__ __forceinline__ void ws_value_step(const Ctx &c, const LaneOffs &lo, const StepIO &io,
+                                              const TileLoads &tl, int64_t &slot_vec,
+                                              int slot_tile, f32x16 *o, const char *xp,
+                                              float &mb) {
+  constexpr int N = 2 * kBBlocks;
+  // the copy's reads first: their latency passes while P is taken and the loads are issued
+  u32x4 craw[kRowsPerWave];
+  const char *cvr = io.kraw + lo.cv_rd;
+  char *cvw = io.vwr + lo.cv_wr;
+  if constexpr (K == kMain) {
+#pragma unroll
+    for (int u = 0; u < kRowsPerWave; ++u)
+      craw[u] = *reinterpret_cast<const u32x4 *>(cvr + kLatStride * u);
+  }
+  f16x8 pf[2];
+  const float mn = ws_take(xp, c.lane, pf);
+  if constexpr (K == kMain) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, tl, io.dma_raw, i);
+    issue_rope(c, tl, io.dma_raw);
+    slot_vec = fetch_slot(c, slot_tile);
+#pragma unroll
+    for (int u = 0; u < kRowsPerWave; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) craw[u][i] = bf16pair_to_f16pair(craw[u][i]);
+      *reinterpret_cast<u32x4 *>(cvw + kVRow * u) = craw[u];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const char *vtr = io.vrd + lo.v_tr;
+  u32x4 fr[kDepthB + 1];
+  auto load = [&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    if constexpr (p < N)
+      fr[p % (kDepthB + 1)] = op_frag<true, p, kABlocks, kBBlocks>(nullptr, nullptr, vtr);
+  };
+  static_for<0, kDepthB>(load);
+  ws_rescale(mn, mb, o);
+  static_for<0, N>([&](auto pc) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    load(std::integral_constant<int, p + kDepthB>{});
+    constexpr int ch = p / kBBlocks, d = p % kBBlocks;
+    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        __builtin_bit_cast(f16x8, fr[p % (kDepthB + 1)]), pf[ch], o[d], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// The fp16 copy of a whole tile (the units this thread staged), with no products beside it.
+__device__ __forceinline__ void ws_convert(const LaneOffs &lo, const char *raw, char *vt) {
+  u32x4 u4[kRowsPerWave];
+#pragma unroll
+  for (int u = 0; u < kRowsPerWave; ++u)
+    u4[u] = *reinterpret_cast<const u32x4 *>(raw + lo.cv_rd + kLatStride * u);
+#pragma unroll
+  for (int u = 0; u < kRowsPerWave; ++u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u4[u][i] = bf16pair_to_f16pair(u4[u][i]);
+    *reinterpret_cast<u32x4 *>(vt + lo.cv_wr + kVRow * u) = u4[u];
+  }
+}
+
+// The hand-over of P(t) and the running max it was computed against (lane l: its P fragment
+// words and its row's max).
+__device__ __forceinline__ void ws_put(char *x, int lane, const f16x8 *pf, float m) {
+  *reinterpret_cast<f16x8 *>(x + 16 * lane) = pf[0];
+  *reinterpret_cast<f16x8 *>(x + 1024 + 16 * lane) = pf[1];
+  *reinterpret_cast<float *>(x + 2048 + 4 * lane) = m;
+}
+
+// int16 codes of output blocks [d0, d0 + n) of this lane's row against the group maximum m
+// (scale factor f = 1 / m, 0 when m is 0); a block's 16 accumulators per lane.
+template <int kN>
+__device__ __forceinline__ void ws_codes(int16_t *pq, int d0, int half, const f32x16 *o,
+                                         float f) {
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    uint32_t cw[4][2];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      cw[gq][0] = snorm16x2(o[i][4 * gq] * f, o[i][4 * gq + 1] * f);
+      cw[gq][1] = snorm16x2(o[i][4 * gq + 2] * f, o[i][4 * gq + 3] * f);
+    }
+    store_codes(pq, d0 + i, half, cw);
+  }
+}
+
+template <int kN>
+__device__ __forceinline__ float lane_absmax(const f32x16 *o) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < kN; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(o[i][e]));
+  return m;
+}
+
+// What both kinds of wavefront know of the item.
+struct WsItem {
+  Ctx c;
+  LaneOffs lo;
+  int ntiles;
+  bool active;   // the row group has rows of the request (wave-uniform)
+  bool row_ok;   // this lane's row is one of them
+  int rho;       // local row
+  int tok;
+  int64_t grow;
+};
+
+// Epilogue exchange (after the last tile): [wave g][lane] floats at x: ltot, the score
+// wavefront's and the value wavefront's group-0 maxima.
+__device__ __forceinline__ float *ws_ex(int g, int k) {
+  return reinterpret_cast<float *>(g_ldsw + kWsXOff) + (3 * g + k) * 64;
+}
+
+template <bool kArgmax>
+__device__ __forceinline__ void ws_score(const RunArgs &a, const Workspace &ws, const Item &it,
+                                         const WsItem &w) {
+  const Ctx &c = w.c;
+  const Segment &seg = it.seg;
+  const int H = a.H;
+  const int rows_req = it.rows;
+  const int row0 = it.rt * kRows;
+  char *const raw0 = g_ldsw;
+  char *const raw1 = g_ldsw + kRawTile;
+  char *const v0 = g_ldsw + kVOff;
+  char *const v1 = g_ldsw + kVOff + kVTile;
+
+  // the query rows, staged through LDS in two halves as in the one-per-SIMD variant
+  constexpr int kQHUnits = kQFrags + 1;
+  constexpr int kQHStride = 16 * kQHUnits;
+  constexpr int kQHChunks = 32 * kQHUnits;
+  constexpr int kQHLoads = (kQHChunks + 63) / 64;
+  char *const qblk = g_ldsw + kVOff + c.wave * 32 * kQHStride;
+  const int64_t row_first = seg.q0 * H + row0 + c.wave * 32;
+  const int64_t row_last = seg.q0 * H + rows_req - 1;
+  const int64_t base_row = min(row_first, row_last);
+  const int nrows = int(min(int64_t(32), row_last - base_row + 1));
+  const uint64_t qbase =
+      uint64_t(reinterpret_cast<uintptr_t>(a.q)) + uint64_t(base_row) * (2 * kDim);
+  const uint32_t qlim = uint32_t(nrows * (2 * kDim) - 16);
+  auto stage_half = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kQHLoads; ++i) {
+      const int ch = 64 * i + c.lane;
+      const uint32_t voff = min(uint32_t(16 * (ch + 35 * (ch / kQHUnits)) + 576 * h), qlim);
+      if (64 * (i + 1) <= kQHChunks || ch < kQHChunks)
+        dma_row(qbase, voff, lds_addr(qblk) + 1024 * i);
+    }
+  };
+  u32x4 qv[kQFrags];
+  auto read_half = [&](int h) __attribute__((always_inline)) {
+    const char *qr = qblk + c.col * kQHStride + 16 * c.half;
+#pragma unroll
+    for (int k = 0; k < kQFrags / 2; ++k)
+      qv[h * (kQFrags / 2) + k] = *reinterpret_cast<const u32x4 *>(qr + 32 * k);
+  };
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of the plan is still in flight
+  stage_half(0);
+  wait_tile_loads();
+  read_half(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  stage_half(1);
+  wait_tile_loads();
+  read_half(1);
+  bf16x8 qf[kQFrags];
+#pragma unroll
+  for (int kc = 0; kc < kQFrags; ++kc) {
+    asm volatile("" : "+v"(qv[kc]));
+    qf[kc] = __builtin_bit_cast(bf16x8, qv[kc]);
+  }
+
+  f32x16 o[kABlocks];
+#pragma unroll
+  for (int d = 0; d < kABlocks; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  RowState st;
+  st.m = -INFINITY;
+  st.mx = -INFINITY;
+  st.lsum = 0.f;
+  st.best_j = -1;
+  const float c2 = a.scale * kLog2e;
+  const uint8_t *mseg = a.mask + seg.m0;
+  const uint32_t moff = uint32_t(w.tok) * uint32_t(seg.L);
+  char *const xb = g_ldsw + kWsXOff + c.wave * kXPair;
+  constexpr int kXPar = kWaves * kXPair;
+
+  f16x8 pf[2];
+  if (w.ntiles > 0) {
+    __syncthreads();  // tile 0 has landed; every query half has been read
+    f32x16 s;
+    if (w.active) {
+      ws_score_step<kFirst>(w.lo, raw0, v0, qf, o, pf, s);
+      score_max<kArgmax, kABlocks, false, true>(c, c.k0, g_okbits[0], s, o, st, c2, w.row_ok, mseg,
+                                          moff);
+      const float negm = neg_max(st);
+#pragma unroll
+      for (int part = 0; part < 8; ++part) p_part(part, s, c2, negm, st.lsum, pf);
+      ws_put(xb, c.lane, pf, st.m);
+    }
+    __syncthreads();
+    for (int t = 0; t + 1 < w.ntiles; ++t) {
+      const int b = t & 1;
+      if (w.active) {
+        ws_score_step<kMain>(w.lo, b ? raw0 : raw1, b ? v1 : v0, qf, o, pf, s);
+        score_max<kArgmax, kABlocks, false, true>(c, c.k0 + (t + 1) * kTK, g_okbits[b ^ 1], s,
+                                                  o, st, c2, w.row_ok, mseg, moff);
+        const float negm = neg_max(st);
+#pragma unroll
+        for (int part = 0; part < 8; ++part) p_part(part, s, c2, negm, st.lsum, pf);
+        ws_put(xb + (b ^ 1) * kXPar, c.lane, pf, st.m);
+      }
+      __syncthreads();
+    }
+    if (w.active) ws_score_step<kLast>(w.lo, raw0, ((w.ntiles - 1) & 1) ? v1 : v0, qf, o, pf, s);
+  }
+  __syncthreads();  // every P has been taken: the exchange area is free
+
+  const float ltot = st.lsum + swap_halves(st.lsum);
+  float ma = 0.f;  // this wavefront's part of the shared scale group
+  if constexpr (kSplit) ma = lane_absmax<kABlocks - 4 * kSplitG>(o + 4 * kSplitG);
+  if (w.active) {
+    ws_ex(c.wave, 0)[c.lane] = ltot;
+    ws_ex(c.wave, 1)[c.lane] = ma;
+  }
+  __syncthreads();
+  if (!w.active || !w.row_ok) return;
+  const int64_t prow = it.prow + int64_t(it.k) * rows_req + w.rho;
+  if (prow >= ws.part_rows) {  // cannot happen: the workspace is sized for every plan
+    atomicOr(ws.status, 2u);   // VA_DEV_SEGMENT
+    return;
+  }
+  if (it.k == 0 && c.half == 0) {
+    RowInfo ri;
+    ri.base = it.prow + w.rho;
+    ri.n = it.n;
+    ri.stride = rows_req;
+    ws.row_info[w.grow] = ri;
+  }
+  int16_t *pq = static_cast<int16_t *>(ws.part_o) + prow * kLatent;
+  const float sl = ltot > 0.f ? 1.f / (32767.f * ltot) : 0.f;
+  float *ps = ws.part_scale + kScaleGroups * prow;
+#pragma unroll
+  for (int g = 0; g < kSplitG; ++g) {
+    float m = lane_absmax<4>(o + 4 * g);
+    m = fmaxf(m, other_half(m));
+    ws_codes<4>(pq, 4 * g, c.half, o + 4 * g, m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f);
+    if (c.half == 0) ps[g] = m * sl;
+  }
+  if constexpr (kSplit) {
+    float m = fmaxf(ma, ws_ex(c.wave, 2)[c.lane]);
+    m = fmaxf(m, other_half(m));
+    ws_codes<kABlocks - 4 * kSplitG>(pq, 4 * kSplitG, c.half, o + 4 * kSplitG,
+                                     m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f);
+    if (c.half == 0) ps[kSplitG] = m * sl;
+  }
+  if (c.half == 0) {
+    const bool any = ltot > 0.f;
+    ws.part_lse[prow] = any ? (st.m + log2f(ltot)) * kLn2 : -INFINITY;
+    ws.part_max[prow] = any ? st.mx * kLn2 : -INFINITY;
+    ws.part_arg[prow] = any && kArgmax ? st.best_j : -1;
+  }
+}
+
+__device__ __forceinline__ void ws_value(const Workspace &ws, const Item &it, const WsItem &w) {
+  const Ctx &c = w.c;
+  const int rows_req = it.rows;
+  char *const raw0 = g_ldsw;
+  char *const raw1 = g_ldsw + kRawTile;
+  char *const v0 = g_ldsw + kVOff;
+  char *const v1 = g_ldsw + kVOff + kVTile;
+  const char *const xb = g_ldsw + kWsXOff + c.wave * kXPair;
+  constexpr int kXPar = kWaves * kXPair;
+
+  int64_t slot_vec = -1;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of the plan is still in flight
+  if (w.ntiles > 0) {
+    load_slots_lds(c, 0);
+    load_slots_lds(c, 1);
+    wait_tile_loads();
+    const TileLoads t0 = plan_tile(c, 0, read_slots(c, 0));
+    const TileLoads t1 = plan_tile(c, 1, read_slots(c, 1));
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, t0, lds_addr(raw0), i);
+    issue_rope(c, t0, lds_addr(raw0));
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) issue_latent(c, t1, lds_addr(raw1), i);
+    issue_rope(c, t1, lds_addr(raw1));
+    publish_ok(c, 0, t0.ok);
+    publish_ok(c, 1, t1.ok);
+    slot_vec = fetch_slot(c, 2);
+  }
+
+  f32x16 o[kBBlocks];
+#pragma unroll
+  for (int d = 0; d < kBBlocks; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.f;
+  float mb = -INFINITY;
+  TileLoads none;
+  none.addr = 0;
+  none.ok = 0;
+  if (w.ntiles > 0) {
+    wait_loads_but_10();  // tile 0 (tile 1 and the slot fetch of tile 2 may be in flight)
+    __syncthreads();
+    ws_convert(w.lo, raw0, v0);
+    wait_tile_loads();
+    __syncthreads();
+    for (int t = 0; t + 1 < w.ntiles; ++t) {
+      const int b = t & 1;
+      const TileLoads tl = plan_tile(c, t + 2, slot_vec);
+      StepIO sio;
+      sio.kraw = b ? raw0 : raw1;
+      sio.vrd = b ? v1 : v0;
+      sio.vwr = b ? v0 : v1;
+      sio.dma_raw = lds_addr(b ? raw1 : raw0);
+      publish_ok(c, b, tl.ok);
+      // (a wavefront whose rows lie past the request runs the same code on a P nobody wrote
+      // and never stores the result: one code path, so that the compiler's wait counting
+      // sees the slot fetch's completion wait rather than a join it must treat as pending)
+      ws_value_step<kMain>(c, w.lo, sio, tl, slot_vec, t + 3, o, xb + b * kXPar, mb);
+      wait_tile_loads();
+      __syncthreads();
+    }
+    {
+      const int b = (w.ntiles - 1) & 1;
+      StepIO eio;
+      eio.kraw = raw0;
+      eio.vrd = b ? v1 : v0;
+      eio.vwr = v0;
+      eio.dma_raw = 0;
+      ws_value_step<kLast>(c, w.lo, eio, none, slot_vec, 0, o, xb + b * kXPar, mb);
+    }
+  }
+  __syncthreads();  // every P has been taken: the exchange area is free
+
+  // this wavefront's part of the scale group it may share with the score wavefront
+  constexpr int kOwn0 = kSplit ? 4 * (kSplitG + 1) - kABlocks : 0;  // its blocks in that group
+  float mb0 = 0.f;
+  if constexpr (kSplit) mb0 = lane_absmax<kOwn0>(o);
+  if (w.active) ws_ex(c.wave, 2)[c.lane] = mb0;
+  __syncthreads();
+  if (!w.active || !w.row_ok) return;
+  const int64_t prow = it.prow + int64_t(it.k) * rows_req + w.rho;
+  if (prow >= ws.part_rows) return;  // reported by the score wavefront
+  const float ltot = ws_ex(c.wave, 0)[c.lane];
+  const float sl = ltot > 0.f ? 1.f / (32767.f * ltot) : 0.f;
+  int16_t *pq = static_cast<int16_t *>(ws.part_o) + prow * kLatent;
+  float *ps = ws.part_scale + kScaleGroups * prow;
+  if constexpr (kSplit) {
+    float m = fmaxf(ws_ex(c.wave, 1)[c.lane], mb0);
+    m = fmaxf(m, other_half(m));
+    ws_codes<kOwn0>(pq, kABlocks, c.half, o, m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f);
+    if (c.half == 0) ps[kSplitG] = m * sl;
+  }
+#pragma unroll
+  for (int g = kSplitG + (kSplit ? 1 : 0); g < kScaleGroups; ++g) {
+    const f32x16 *og = o + 4 * g - kABlocks;
+    float m = lane_absmax<4>(og);
+    m = fmaxf(m, other_half(m));
+    ws_codes<4>(pq, 4 * g, c.half, og, m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f);
+    if (c.half == 0) ps[g] = m * sl;
+  }
+}
+
+template <bool kArgmax>
+__device__ __forceinline__ void run_item_ws(const RunArgs &a, const Workspace &ws,
+                                            const Item &it) {
+  const Segment &seg = it.seg;
+  const int H = a.H;
+  const int rows_req = it.rows;
+  const int row0 = it.rt * kRows;
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+
+  WsItem w;
+  Ctx &c = w.c;
+  c.kv = static_cast<const uint16_t *>(a.kv);
+  c.kvi = a.kv_indices + seg.kv0;
+  c.tree = seg.tree;
+  c.zero = ws.zero_row;
+  c.num_slots = a.num_slots;
+  c.status = ws.status;
+  c.P = seg.P;
+  c.wave = wv & (kWaves - 1);
+  c.lane = int(threadIdx.x) & 63;
+  c.half = c.lane >> 5;
+  c.col = c.lane & 31;
+  w.rho = row0 + c.wave * 32 + c.col;
+  w.row_ok = w.rho < rows_req;
+  w.active = row0 + c.wave * 32 < rows_req;
+  const int rho_c = w.row_ok ? w.rho : rows_req - 1;
+  w.tok = rho_c / H;
+  w.grow = (seg.q0 + w.tok) * int64_t(H) + rho_c % H;
+  split_range(seg.L, it.k, it.n, c.k0, c.k1);
+  w.ntiles = (c.k1 - c.k0 + kTK - 1) / kTK;
+  w.lo = lane_offsets(c);
+  if (wv < kWaves)
+    ws_score<kArgmax>(a, ws, it, w);
+  else
+    ws_value(ws, it, w);
+}
+
+template <bool kArgmax>
+__global__ void __launch_bounds__(kWsThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+mfma_partial_ws_kernel(RunArgs a, Workspace ws, int G) {
+  const int nb = gridDim.x;
+  const int lane = int(threadIdx.x) & 63;
+  const int64_t w = (int(blockIdx.x) & 7) * (nb >> 3) + (int(blockIdx.x) >> 3);
+  Item it;
+  {
+    const ReqWork mine = req_work(a, lane);
+    const WorkPlan plan = plan_work(a, mine, G, ws.splits, ws.status,
+                                    blockIdx.x == 0 && threadIdx.x < 64, lane);
+    if (w >= plan.items || !find_item<true>(a, mine, plan, w, lane, it)) return;
+  }
+  // (an item of 32 rows or fewer cannot occur: the launch takes this kernel only for H a
+  // multiple of 64)
+  if (it.rows - it.rt * kRows <= 32) {
+    if (threadIdx.x == 0) atomicOr(ws.status, 2u);  // VA_DEV_SEGMENT
+    return;
+  }
+  run_item_ws<kArgmax>(a, ws, it);
+}
+
 template <bool kArgmax>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -1478,12 +2056,20 @@ hipError_t launch_mfma_partial(const RunArgs &a, const Workspace &ws, int rows_p
   int64_t nb = std::max(int64_t(work_items), int64_t(a.bs) * tiles * per_tile);
   nb = (nb + 7) / 8 * 8;
   if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (a.want_argmax)
+  if (mfma_partial_waves(a.H) == 8) {  // no item of 32 rows or fewer: two per SIMD
+    if (a.want_argmax)
+      hipLaunchKernelGGL(mfma_partial_ws_kernel<true>, dim3(unsigned(nb)), dim3(kWsThreads), 0,
+                         st, a, ws, work_items);
+    else
+      hipLaunchKernelGGL(mfma_partial_ws_kernel<false>, dim3(unsigned(nb)), dim3(kWsThreads), 0,
+                         st, a, ws, work_items);
+  } else if (a.want_argmax) {
     hipLaunchKernelGGL(mfma_partial_kernel<true>, dim3(unsigned(nb)), dim3(kThreads), 0, st, a,
                        ws, work_items);
-  else
+  } else {
     hipLaunchKernelGGL(mfma_partial_kernel<false>, dim3(unsigned(nb)), dim3(kThreads), 0, st, a,
                        ws, work_items);
+  }
   return hipGetLastError();
 }
 

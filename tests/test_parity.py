@@ -166,6 +166,28 @@ def test_many_heads(kernel):
     compare(w, run_gpu(w, kernel=kernel), ref)
 
 
+def test_partial_variant_follows_num_heads():
+    """The MFMA partial workgroup runs 8 wavefronts (two per SIMD) exactly when H is a multiple
+    of 64, so that no work item has 32 rows or fewer; otherwise 4. The fp32 kernel runs 4."""
+    from mla_tree_verify_paged_amd import VerifyAttn
+    for h, waves in ((64, 8), (128, 8), (192, 8), (8, 4), (16, 4), (48, 4), (96, 4)):
+        va = VerifyAttn(h, max_batch=2, max_q_per_req=4, max_q_tokens=8, kernel="mfma")
+        assert va.info.partial_waves == waves, (h, va.info.partial_waves)
+    va = VerifyAttn(64, in_dtype="fp32", max_batch=1, max_q_per_req=4, max_q_tokens=4)
+    assert va.info.partial_waves == 4
+
+
+@pytest.mark.parametrize("kernel", BF16_KERNELS)
+def test_eight_wave_half_tiles(kernel):
+    """H = 64 with odd tree sizes: requests of 1, 3 and 5 tokens end in a 64-row tile whose last
+    two row groups lie past the request (their wavefronts stage and compute but never store),
+    with empty, one-tile and many-tile prefixes."""
+    rng = np.random.default_rng(21)
+    w = wl.build_workload("half64", rng, 64, [0, 33, 1500, 95], [1, 3, 5, 2], 4096)
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel=kernel), ref)
+
+
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
 def test_large_tree(kernel):
     """A 384-node draft tree at H = 8 (3072 rows: the wavefront-per-row combine) over a short
