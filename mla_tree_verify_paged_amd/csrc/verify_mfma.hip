@@ -25,12 +25,17 @@
 //    per tile (each thread converts the units it loaded) and read as V^T fragments with
 //    ds_read_b64_tr_b16. The P fragment is the S accumulator itself: key slots are permuted
 //    the same way in both operands;
-//  * the tile loop is software-pipelined: the P.V products of tile t are interleaved with the
-//    QK^T products of tile t+1 (so the scores of tile t+1 are ready when tile t's products
-//    end), with the fp16 conversion of tile t+1 and the loads of tile t+2 slotted between
-//    them. With one wavefront per SIMD (the 256 output accumulators per lane rule out more)
-//    the other instructions issue between the matrix instructions rather than beside them, so
-//    the loop is written to issue as few as possible;
+//  * the tile loop is software-pipelined: the P.V products of tile t and the QK^T products of
+//    tile t+1 run in one step (so the scores of tile t+1 are ready when tile t's products
+//    end), with the fp16 conversion of tile t+1 and the loads of tile t+2 beside them;
+//  * two variants share all of the above. With H a multiple of 64 a workgroup runs eight
+//    wavefronts, two per SIMD (section "two wavefronts per SIMD" below): four hold the query
+//    rows and do the scores and softmax, four hold three quarters of the output accumulators
+//    and stage the tiles, so one wavefront's vector and LDS work issues while the other's
+//    matrix instructions run. Otherwise four wavefronts of 32 rows each hold all 256 output
+//    accumulators per lane, one wavefront per SIMD, and every other instruction issues
+//    between their matrix instructions, so that loop is written to issue as few as possible
+//    (it also has the path for items of at most 32 rows);
 //  * the running max is rescaled lazily (only when it grows by more than 2^8), in place in
 //    the accumulation registers, so the 256 fp32 accumulators per lane never leave them;
 //  * workgroups are mapped so that all row tiles of one key split run on the same XCD and
