@@ -94,60 +94,65 @@ def test_fuzz_small_shapes(kernel, seed):
 
 # ----------------------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
-def test_zero_prefix_and_single_token(kernel):
+@pytest.mark.parametrize("h", [8, 64])  # the 4- and the 8-wavefront partial kernel
+def test_zero_prefix_and_single_token(kernel, h):
     rng = np.random.default_rng(7)
-    w = wl.build_workload("p0", rng, 8, [0, 0, 5], [1, 7, 1], 64)
+    w = wl.build_workload("p0", rng, h, [0, 0, 5], [1, 7, 1], 64)
     ref = run_oracle(w)
     compare(w, run_gpu(w, kernel=kernel), ref)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
-def test_more_splits_than_keys(kernel):
+@pytest.mark.parametrize("h", [16, 64])
+def test_more_splits_than_keys(kernel, h):
     rng = np.random.default_rng(8)
-    w = wl.build_workload("split", rng, 16, [3, 40], [2, 5], 128)
+    w = wl.build_workload("split", rng, h, [3, 40], [2, 5], 128)
     ref = run_oracle(w)
     compare(w, run_gpu(w, kernel=kernel, num_splits=64), ref)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
-def test_fully_masked_rows_are_empty(kernel):
+@pytest.mark.parametrize("h", [4, 64])
+def test_fully_masked_rows_are_empty(kernel, h):
     rng = np.random.default_rng(9)
-    w = wl.build_workload("masked", rng, 4, [0], [6], 32)
+    w = wl.build_workload("masked", rng, h, [0], [6], 32)
     m = w.custom_mask.reshape(6, 6)
     m[2, :] = 0
     m[4, :] = 0
     ref = run_oracle(w)
     o, l, a, st = run_gpu(w, kernel=kernel)
     for tok in (2, 4):
-        rows = slice(tok * 4, tok * 4 + 4)
+        rows = slice(tok * h, tok * h + h)
         assert np.all(o[rows] == 0) and np.all(l[rows] == -np.inf) and np.all(a[rows] == -1)
     compare(w, (o, l, a, st), ref)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
-def test_request_without_tree_tokens(kernel):
+@pytest.mark.parametrize("h", [8, 64])
+def test_request_without_tree_tokens(kernel, h):
     rng = np.random.default_rng(10)
-    w = wl.build_workload("t0", rng, 8, [50, 30, 70], [3, 0, 4], 256)
+    w = wl.build_workload("t0", rng, h, [50, 30, 70], [3, 0, 4], 256)
     ref = run_oracle(w)
     compare(w, run_gpu(w, kernel=kernel), ref)
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
-def test_empty_batches_write_nothing(kernel):
+@pytest.mark.parametrize("h", [8, 64])
+def test_empty_batches_write_nothing(kernel, h):
     """bs = 0, and a batch whose requests all have T_r = 0 (num_tokens = 0): the call succeeds,
     enqueues nothing that writes, and leaves the output buffers as they were."""
     import torch
     from mla_tree_verify_paged_amd import VerifyAttn
     from mla_tree_verify_paged_amd.device_inputs import to_device
     rng = np.random.default_rng(11)
-    w = wl.build_workload("t0all", rng, 8, [40, 0, 25], [0, 0, 0], 128)
+    w = wl.build_workload("t0all", rng, h, [40, 0, 25], [0, 0, 0], 128)
     assert w.num_tokens == 0
     dev = to_device(w)
-    va = VerifyAttn(8, max_batch=4, max_q_per_req=4, max_q_tokens=8, kernel=kernel)
-    q = torch.zeros((8, 8, 576), dtype=torch.bfloat16, device="cuda")
-    out = torch.full((8, 8, 512), 3.0, device="cuda")
-    lse = torch.full((8, 8), 5.0, device="cuda")
-    am = torch.full((8, 8), 7, dtype=torch.int32, device="cuda")
+    va = VerifyAttn(h, max_batch=4, max_q_per_req=4, max_q_tokens=8, kernel=kernel)
+    q = torch.zeros((8, h, 576), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((8, h, 512), 3.0, device="cuda")
+    lse = torch.full((8, h), 5.0, device="cuda")
+    am = torch.full((8, h), 7, dtype=torch.int32, device="cuda")
     for bs in (0, w.bs):
         va.run(q, dev["kv_buffer"], dev["kv_indices"], dev["kv_indptr"], dev["qo_indptr"],
                dev["custom_mask"], dev["mask_indptr"], w.scale, out, lse, am, bs=bs,
@@ -390,13 +395,14 @@ def test_value_groups_at_different_scales(kernel, shape):
 # ----------------------------------------------------------------------------- argmax tie rule
 @pytest.mark.parametrize("kernel", BF16_KERNELS)
 @pytest.mark.parametrize("splits", [0, 8])
-def test_argmax_tie_across_splits_goes_to_the_lower_key(kernel, splits):
+@pytest.mark.parametrize("h", [4, 64])
+def test_argmax_tie_across_splits_goes_to_the_lower_key(kernel, splits, h):
     """One slot appears at key positions 300 and 2800 (in different key splits) and holds a
     row aligned with every query, so both positions attain the maximum with bit-identical
     scores: the argmax must be the lower position, 300 (the oracle's rule, pinned there by
     brute force)."""
     rng = np.random.default_rng(40)
-    h, p, t = 4, 3000, 2
+    p, t = 3000, 2
     w = wl.build_workload("tie", rng, h, [p], [t], 8192)
     q = wl.bf16_bits_to_f32(w.q)
     q[:, :, :] = q[0, 0]                       # every row has the same query

@@ -15,11 +15,12 @@ KERNELS = ["simple", "mfma"]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_out_of_range_slot_is_ignored_and_flagged(kernel):
-    w = wl.build_workload("slot", np.random.default_rng(20), 8, [40], [4], 128)
+@pytest.mark.parametrize("h", [8, 64])  # the 4- and the 8-wavefront partial kernel
+def test_out_of_range_slot_is_ignored_and_flagged(kernel, h):
+    w = wl.build_workload("slot", np.random.default_rng(20), h, [40], [4], 128)
     p = 40
     # reference: tree key 3 hidden from every query
-    ref_w = wl.build_workload("slot", np.random.default_rng(20), 8, [40], [4], 128)
+    ref_w = wl.build_workload("slot", np.random.default_rng(20), h, [40], [4], 128)
     ref_w.custom_mask.reshape(4, 44)[:, p + 3] = 0
     ref = run_oracle(ref_w)
     w.kv_indices[p + 3] = w.num_slots + 5
@@ -33,26 +34,28 @@ def test_out_of_range_slot_is_ignored_and_flagged(kernel):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_too_many_tree_tokens_for_the_context(kernel):
-    w = wl.build_workload("tq", np.random.default_rng(21), 8, [30, 30], [3, 9], 128)
+@pytest.mark.parametrize("h", [8, 64])
+def test_too_many_tree_tokens_for_the_context(kernel, h):
+    w = wl.build_workload("tq", np.random.default_rng(21), h, [30, 30], [3, 9], 128)
     o, l, a, st = run_gpu(w, kernel=kernel, max_q_per_req=4, max_q_tokens=12)
     assert st & B.VA_DEV_Q_PER_REQ
     ref = run_oracle(w)
-    first = 3 * 8
+    first = 3 * h
     compare(w, (o, l, a, 0), (ref[0][:first], ref[1][:first], ref[2][:first]),
             rows=np.arange(first))
     assert np.all(o[first:] == 0) and np.all(l[first:] == -np.inf) and np.all(a[first:] == -1)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_prefix_shorter_than_tree_is_flagged(kernel):
-    w = wl.build_workload("seg", np.random.default_rng(22), 4, [10, 20], [4, 4], 128)
+@pytest.mark.parametrize("h", [4, 64])
+def test_prefix_shorter_than_tree_is_flagged(kernel, h):
+    w = wl.build_workload("seg", np.random.default_rng(22), h, [10, 20], [4, 4], 128)
     from mla_tree_verify_paged_amd.device_inputs import to_device
     dev = to_device(w)
     dev["kv_indptr"][1] = 2          # request 0: L=2 < T=4; request 1: L=32
     o, l, a, st = run_gpu(w, kernel=kernel, dev=dev)
     assert st & B.VA_DEV_SEGMENT
-    assert np.all(o[:16] == 0) and np.all(l[:16] == -np.inf)
+    assert np.all(o[:4 * h] == 0) and np.all(l[:4 * h] == -np.inf)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
