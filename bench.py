@@ -249,23 +249,25 @@ def lds_probe():
     lib = ctypes.CDLL(os.path.join(ROOT, "mla_tree_verify_paged_amd", "liblds_mfma_probe.so"))
     lib.lds_mfma_probe.argtypes = [ctypes.POINTER(ctypes.c_double)]
     lib.lds_mfma_probe.restype = ctypes.c_int
-    out = (ctypes.c_double * 20)()
+    out = (ctypes.c_double * 28)()
     rc = lib.lds_mfma_probe(out)
     if rc != 0:
         return {"error": f"hip error {rc}"}
     forms = ["b128 (K fragment)", "two tr_b64 (V^T fragment)", "alternating",
-             "b128 + two tr_b64 (2 KB per product)"]
+             "b128 + two tr_b64 (2 KB per product)", "two b128 (2 KB per product)",
+             "four tr_b64 (2 KB per product)"]
+    nf = len(forms)
     feed = {}
     for w in range(2):
         for f, name in enumerate(forms):
             feed.setdefault(name, {})[f"{w + 1} wave/SIMD"] = {
-                "mfma_util_pct": round(out[8 * w + 2 * f], 1),
-                "lds_bytes_per_clk_per_cu": round(out[8 * w + 2 * f + 1], 1)}
+                "mfma_util_pct": round(out[2 * nf * w + 2 * f], 1),
+                "lds_bytes_per_clk_per_cu": round(out[2 * nf * w + 2 * f + 1], 1)}
     return {"feed": feed,
-            "cycles_per_32x32x16_product": {"1 chain": round(out[16], 2),
-                                            "2 chains": round(out[17], 2),
-                                            "4 chains": round(out[18], 2)},
-            "clock_ghz": round(out[19], 2),
+            "cycles_per_32x32x16_product": {"1 chain": round(out[4 * nf], 2),
+                                            "2 chains": round(out[4 * nf + 1], 2),
+                                            "4 chains": round(out[4 * nf + 2], 2)},
+            "clock_ghz": round(out[4 * nf + 3], 2),
             "method": "one 256- or 512-thread workgroup per CU (96 KB LDS), each product's 1 KB "
                       "operand read 4 products ahead; utilisation = matrix cycles / elapsed "
                       "cycles"}

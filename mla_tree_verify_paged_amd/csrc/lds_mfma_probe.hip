@@ -7,7 +7,9 @@
 //    instructions earlier, in the read forms the kernel uses: one ds_read_b128 per
 //    instruction (the K-fragment pattern, 1040-byte rows), two ds_read_b64_tr_b16 (the V^T
 //    pattern, 1088-byte rows), the two alternating, or both per instruction (2 KB per 32
-//    cycles of matrix work, the operand ratio of a 16-row wavefront);
+//    cycles of matrix work, the operand ratio of a 16-row wavefront); and, to tell the two
+//    read forms' LDS rates apart where LDS rather than the matrix core sets the pace, 2 KB per
+//    instruction of one form only: two b128 reads, or four transposing reads;
 //  * one workgroup per compute unit (a 96 KB LDS array forces it) of 256 threads (one
 //    wavefront per SIMD) or 512 threads (two);
 //  * matrix-core utilisation = matrix cycles per SIMD / the workgroup's elapsed cycles (first
@@ -32,7 +34,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kLdsBytes = 96 * 1024;
 constexpr int kVOff = 40960;  // the V^T-pattern region
 
-enum Form { kB128 = 0, kTr = 1, kAlt = 2, kBoth = 3 };
+enum Form { kB128 = 0, kTr = 1, kAlt = 2, kBoth = 3, kB128x2 = 4, kTrx2 = 5 };
+constexpr int kForms = 6;
 
 // The operand of instruction k: K pattern (row lane % 32 at a 1040-byte stride, 16 bytes per
 // lane) or V^T pattern (two transposing reads, rows at a 1088-byte stride). Offsets stay
@@ -58,7 +61,10 @@ __device__ __forceinline__ u32x4 operand(const char *lds, int lane, int k) {
   if constexpr (F == kB128) return k_read(lds, lane, k);
   else if constexpr (F == kTr) return v_read(lds, lane, k);
   else if constexpr (F == kAlt) return (K & 1) ? v_read(lds, lane, k) : k_read(lds, lane, k);
-  else return k_read(lds, lane, k) ^ v_read(lds, lane, k);
+  else if constexpr (F == kBoth) return k_read(lds, lane, k) ^ v_read(lds, lane, k);
+  // the second b128 read: the same pattern in the V region (offsets below kVOff + 34 KB)
+  else if constexpr (F == kB128x2) return k_read(lds, lane, k) ^ k_read(lds + kVOff, lane, k + 7);
+  else return v_read(lds, lane, k) ^ v_read(lds, lane, k ^ 1);
 }
 
 constexpr int kD = 4;  // operand reads in flight
@@ -174,11 +180,11 @@ struct Buffers {
 
 }  // namespace
 
-// Fills out[0..15] with (matrix-core utilisation %, LDS bytes per clock per compute unit) for
-// the forms b128, two tr reads, alternating, and both per instruction, at one wavefront per
-// SIMD (out[0..7]) and at two (out[8..15]); out[16..18]: cycles per product with 1, 2 and 4
-// accumulation chains; out[19]: the clock in GHz during the last feed measurement. Returns 0
-// or a hipError_t code.
+// Fills out[0..23] with (matrix-core utilisation %, LDS bytes per clock per compute unit) for
+// the forms b128, two tr reads, alternating, b128 + two tr reads, two b128 reads and four tr
+// reads per instruction, at one wavefront per SIMD (out[0..11]) and at two (out[12..23]);
+// out[24..26]: cycles per product with 1, 2 and 4 accumulation chains; out[27]: the clock in
+// GHz during the last feed measurement. Returns 0 or a hipError_t code.
 extern "C" int lds_mfma_probe(double *out) {
   Buffers buf;
   hipError_t e = hipMalloc(&buf.sink, size_t(kBlocks) * 512 * sizeof(float));
@@ -187,7 +193,7 @@ extern "C" int lds_mfma_probe(double *out) {
   static unsigned long long h[4 * kBlocks * 8];
   for (int w = 0; w < 2; ++w) {
     const int threads = 256 * (w + 1), waves = threads / 64;
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < kForms; ++f) {
       float *sink = buf.sink;
       unsigned long long *dcyc = buf.dcyc;
       auto launch = [&]() {
@@ -195,7 +201,10 @@ extern "C" int lds_mfma_probe(double *out) {
         if (f == kB128) hipLaunchKernelGGL(feed_kernel<kB128>, g, t, 0, 0, sink, dcyc, kIters);
         else if (f == kTr) hipLaunchKernelGGL(feed_kernel<kTr>, g, t, 0, 0, sink, dcyc, kIters);
         else if (f == kAlt) hipLaunchKernelGGL(feed_kernel<kAlt>, g, t, 0, 0, sink, dcyc, kIters);
-        else hipLaunchKernelGGL(feed_kernel<kBoth>, g, t, 0, 0, sink, dcyc, kIters);
+        else if (f == kBoth) hipLaunchKernelGGL(feed_kernel<kBoth>, g, t, 0, 0, sink, dcyc, kIters);
+        else if (f == kB128x2)
+          hipLaunchKernelGGL(feed_kernel<kB128x2>, g, t, 0, 0, sink, dcyc, kIters);
+        else hipLaunchKernelGGL(feed_kernel<kTrx2>, g, t, 0, 0, sink, dcyc, kIters);
       };
       if ((e = run_twice(launch, buf.dcyc, h, 4 * kBlocks * 8)) != hipSuccess) return int(e);
       // per workgroup: first start to last end over its wavefronts (one counter per CU)
@@ -215,11 +224,11 @@ extern "C" int lds_mfma_probe(double *out) {
       }
       cycles /= kBlocks;
       ticks /= kBlocks;
-      out[19] = ticks > 0 ? cycles / (ticks * 10.0) : 0.0;  // the real-time counter is 100 MHz
+      out[27] = ticks > 0 ? cycles / (ticks * 10.0) : 0.0;  // the real-time counter is 100 MHz
       const double mfma_cycles = double(waves) / 4 * kIters * 16 * 32;  // per SIMD
-      const double kb = f == kBoth ? 2.0 : 1.0;
-      out[8 * w + 2 * f] = 100.0 * mfma_cycles / cycles;
-      out[8 * w + 2 * f + 1] = kb * 1024.0 * waves * kIters * 16 / cycles;
+      const double kb = f >= kBoth ? 2.0 : 1.0;
+      out[2 * kForms * w + 2 * f] = 100.0 * mfma_cycles / cycles;
+      out[2 * kForms * w + 2 * f + 1] = kb * 1024.0 * waves * kIters * 16 / cycles;
     }
   }
   for (int c = 0; c < 3; ++c) {
@@ -235,7 +244,7 @@ extern "C" int lds_mfma_probe(double *out) {
     if ((e = run_twice(launch, buf.dcyc, h, kBlocks * 4)) != hipSuccess) return int(e);
     double cycles = 0;
     for (int i = 0; i < kBlocks * 4; ++i) cycles += double(h[i]);
-    out[16 + c] = cycles / (kBlocks * 4) / (kIters * 16.0);
+    out[4 * kForms + c] = cycles / (kBlocks * 4) / (kIters * 16.0);
   }
   return 0;
 }
