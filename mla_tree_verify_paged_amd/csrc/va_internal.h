@@ -115,10 +115,12 @@ struct Segment {
   const int64_t *tree;
 };
 
-__device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segment &s) {
-  const int64_t q0 = a.qo_indptr[r], q1 = a.qo_indptr[r + 1];
-  const int64_t k0 = a.kv_indptr[r], k1 = a.kv_indptr[r + 1];
-  const int64_t m0 = a.mask_indptr[r];
+// Request r's segment from its index-table entries qo_indptr[r], qo_indptr[r + 1],
+// kv_indptr[r], kv_indptr[r + 1] and mask_indptr[r]; returns the VA_DEV_* bits of an unusable
+// segment (then T = L = P = 0), else 0.
+__device__ __forceinline__ uint32_t check_segment(const RunArgs &a, int64_t q0, int64_t q1,
+                                                  int64_t k0, int64_t k1, int64_t m0,
+                                                  Segment &s) {
   s.q0 = q0;
   s.kv0 = k0;
   s.m0 = m0;
@@ -139,6 +141,11 @@ __device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segmen
   s.P = int32_t(L - T);
   if (a.out_cache_loc) s.tree = a.out_cache_loc + q0;
   return 0u;
+}
+
+__device__ __forceinline__ uint32_t load_segment(const RunArgs &a, int r, Segment &s) {
+  return check_segment(a, a.qo_indptr[r], a.qo_indptr[r + 1], a.kv_indptr[r],
+                       a.kv_indptr[r + 1], a.mask_indptr[r], s);
 }
 
 // Arguments of the mask build (see include/verify_attn.h).

@@ -64,6 +64,45 @@ __device__ __forceinline__ int owner_request(const RunArgs &a, int64_t t, int la
   return owner;
 }
 
+// The index-table entries of requests 0..63 (lane l: request l's qo_indptr[l], qo_indptr[l+1],
+// kv_indptr[l], kv_indptr[l+1], mask_indptr[l]), requested at a kernel's start beside the
+// row's placement, so that validating a row costs no round trip of its own. Batches of more
+// than 64 requests read nothing here and validate from the tables (owner_request, then
+// load_segment).
+struct SegTables {
+  int64_t q0, q1, m0;
+  int32_t k0, k1;
+};
+__device__ __forceinline__ SegTables prefetch_tables(const RunArgs &a, int lane) {
+  SegTables p;
+  p.q0 = p.q1 = p.m0 = 0;
+  p.k0 = p.k1 = 0;
+  if (a.bs <= 64 && lane < a.bs) {
+    p.q0 = a.qo_indptr[lane];
+    p.q1 = a.qo_indptr[lane + 1];
+    p.k0 = a.kv_indptr[lane];
+    p.k1 = a.kv_indptr[lane + 1];
+    p.m0 = a.mask_indptr[lane];
+  }
+  return p;
+}
+__device__ __forceinline__ int64_t lane_value(int64_t v, int src) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), src));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint64_t(v) >> 32), src));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+// The segment of the request that owns token t (the same request owner_request picks) and
+// its VA_DEV_* bits. Wave-uniform.
+__device__ __forceinline__ uint32_t owner_segment(const RunArgs &a, const SegTables &p,
+                                                  int64_t t, int lane, Segment &seg) {
+  if (a.bs > 64) return load_segment(a, owner_request(a, t, lane), seg);
+  const uint64_t le = __ballot(lane < a.bs && p.q0 <= t);
+  const int r = le ? 63 - __builtin_clzll(le) : 0;
+  return check_segment(a, lane_value(p.q0, r), lane_value(p.q1, r),
+                       __builtin_amdgcn_readlane(p.k0, r), __builtin_amdgcn_readlane(p.k1, r),
+                       lane_value(p.m0, r), seg);
+}
+
 // the 4 output dims [dim0, dim0 + 4) of `row`
 __device__ void store4(const RunArgs &a, int64_t row, int dim0, const float4 &v) {
   if (a.out_bf16) {
@@ -139,6 +178,8 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   const int group_a = dim_a / kScaleGroupDims;
   const int group_b = kSlices == 1 ? (dim_a + 256) / kScaleGroupDims : group_a;
 
+  // the tables that validate the row, requested before its placement (one round trip for both)
+  const SegTables tabs = prefetch_tables(a, lane);
   // where this row's partials are (written by the partial kernel for every row of a valid
   // request; for other rows it is stale or arbitrary, so it is only used once checked to stay
   // inside the workspace, and such rows are discarded below)
@@ -229,7 +270,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   bool ok = a.bs > 0 && row < a.num_tokens * a.H;
   if (ok) {
     Segment seg;
-    bad = load_segment(a, owner_request(a, t, lane), seg);
+    bad = owner_segment(a, tabs, t, lane, seg);
     ok = bad == 0 && t >= seg.q0 && t < seg.q0 + seg.T;
     if (bad == 0 && !ok) bad = 8u;  // VA_DEV_TOKENS
     if (ok && !placed) {  // cannot happen: the partial kernel places every valid row
@@ -368,6 +409,7 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
   const int64_t t = row / a.H;
   const int dim_a = slice * kScaleGroupDims + 2 * lane;
 
+  const SegTables tabs = prefetch_tables(a, lane);
   // where this row's partials are (checked to stay inside the workspace, as above)
   const RowInfo ri = ws.row_info[row];
   int S = ri.n;
@@ -408,7 +450,7 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
   bool ok = a.bs > 0 && row < a.num_tokens * a.H;
   if (ok) {
     Segment seg;
-    bad = load_segment(a, owner_request(a, t, lane), seg);
+    bad = owner_segment(a, tabs, t, lane, seg);
     ok = bad == 0 && t >= seg.q0 && t < seg.q0 + seg.T;
     if (bad == 0 && !ok) bad = 8u;  // VA_DEV_TOKENS
     if (ok && !placed) {  // cannot happen: the partial kernel places every valid row
@@ -503,6 +545,7 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(RunArgs a, Works
   const int dim_a = 4 * lane;
   const int ga = dim_a / kScaleGroupDims, gb = (dim_a + 256) / kScaleGroupDims;
 
+  const SegTables tabs = prefetch_tables(a, lane);
   const RowInfo ri = ws.row_info[row];
   int S = ri.n;
   int64_t base = ri.base, stride = ri.stride;
@@ -546,7 +589,7 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(RunArgs a, Works
   bool ok = a.bs > 0;
   if (ok) {
     Segment seg;
-    bad = load_segment(a, owner_request(a, t, lane), seg);
+    bad = owner_segment(a, tabs, t, lane, seg);
     ok = bad == 0 && t >= seg.q0 && t < seg.q0 + seg.T;
     if (bad == 0 && !ok) bad = 8u;  // VA_DEV_TOKENS
     if (ok && !placed) {  // cannot happen: the partial kernel places every valid row
