@@ -32,15 +32,33 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// Cross-lane moves without LDS round trips: a DPP operand (kCtrl: quad_perm 0xB1 = lane ^ 1,
+// 0x4E = lane ^ 2; 0x141 = mirrored within 8 lanes, 0x140 = mirrored within 16), and lane l's
+// value read into a scalar register (l wave-uniform).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Wavefront max and sum: a butterfly within each 16-lane row (each step leaves groups of 2,
+// 4, 8, 16 lanes equal), then the four rows' values. Every lane gets the same result, and so
+// does every wavefront that holds the same values in the same lanes.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -168,6 +186,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   __shared__ float red[kWaves - 1][kV][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // the same, in a scalar register
   const int64_t row = blockIdx.x / kSlices;
   const int slice = int(blockIdx.x % kSlices);
   const int64_t t = row / a.H;
@@ -339,7 +358,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
       W += wave_sum(wgt);
       if (arg < 0) {  // wave-uniform: the lowest split holding the largest max score
         const uint64_t hit = __ballot(s < S && mx == best);
-        if (hit) arg = __shfl(ag, int(__builtin_ctzll(hit)), 64);
+        if (hit) arg = __builtin_amdgcn_readlane(ag, int(__builtin_ctzll(hit)));
       }
       // this wavefront's splits of the 64: s0 + wave + 4j, in batches of kBatch
 #pragma unroll 1
@@ -354,8 +373,8 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-          const int sl = wave + kWaves * (j0 + j);  // lane of this split within the 64
-          const float wk = __shfl(wgt, sl, 64);
+          const int sl = wv + kWaves * (j0 + j);  // lane of this split within the 64
+          const float wk = lane_f(wgt, sl);
           // a split with zero weight contributes nothing (its row may be unwritten)
           if (s0 + sl < S && wk != 0.f) {
             const float f0 = wk * x[j].scale(0), f1 = wk * x[j].scale(kV - 1);
@@ -404,6 +423,7 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
   __shared__ float red[kWaves - 1][2][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // the same, in a scalar register
   const int64_t row = blockIdx.x / kSlices;
   const int slice = int(blockIdx.x % kSlices);
   const int64_t t = row / a.H;
@@ -484,7 +504,7 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
 #pragma unroll
   for (int i = kScal - 1; i >= 0; --i) {
     const uint64_t hit = __ballot(mxv[i] == best);
-    if (hit) arg = __shfl(agv[i], int(__builtin_ctzll(hit)), 64);
+    if (hit) arg = __builtin_amdgcn_readlane(agv[i], int(__builtin_ctzll(hit)));
   }
   float W = 0.f, acc0 = 0.f, acc1 = 0.f;
   if (M != -INFINITY) {
@@ -501,11 +521,10 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
       // split wave + 4j: its scalars are in lane (wave + 4j) % 64, slot 4j / 64
-      const float fk = __shfl(f[(kWaves * j) / 64], (wave + kWaves * j) & 63, 64);
-      if (fk != 0.f) {
-        acc0 = fmaf(fk, float(int32_t(cw[j] << 16) >> 16), acc0);
-        acc1 = fmaf(fk, float(int32_t(cw[j]) >> 16), acc1);
-      }
+      // (no zero test: a split without weight has a factor of exactly 0 and finite codes)
+      const float fk = lane_f(f[(kWaves * j) / 64], (wv + kWaves * j) & 63);
+      acc0 = fmaf(fk, float(int32_t(cw[j] << 16) >> 16), acc0);
+      acc1 = fmaf(fk, float(int32_t(cw[j]) >> 16), acc1);
     }
   }
   // the four wavefronts' sums meet in LDS; wavefront 0 finishes the slice
@@ -641,14 +660,14 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(RunArgs a, Works
       W += wave_sum(wgt);
       if (arg < 0) {  // the lowest split holding the largest max score
         const uint64_t hit = __ballot(sp < S && mx == best);
-        if (hit) arg = __shfl(ag, int(__builtin_ctzll(hit)), 64);
+        if (hit) arg = __builtin_amdgcn_readlane(ag, int(__builtin_ctzll(hit)));
       }
 #pragma unroll 1
       for (int j0 = 0; j0 < 64 && s0 + j0 < S; j0 += kB) {
         if (s0 > 0 || j0 > 0) load(s0 + j0);
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
-          const float wk = __shfl(wgt, j0 + j, 64);
+          const float wk = lane_f(wgt, j0 + j);
           // a split with zero weight contributes nothing (its codes may be unwritten)
           if (s0 + j0 + j < S && wk != 0.f) {
             const float fa = wk * sa[j], fb = wk * sb[j];
