@@ -408,26 +408,34 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
   }
 }
 
-// Steps with fewer than 512 rows, 16-bit partials: a quarter row per workgroup (lane l owns
-// dims 2l, 2l+1 of the slice's 128-dim scale group), and every split's codes requested in one
-// round trip. Such rows have many splits (tp8: 240), which the general kernel above reads 16
-// per wavefront per round trip. Wavefront w reads the codes of splits w + 4j (j < 64); lane s
-// holds the scalars of splits s, s + 64, s + 128, s + 192 and folds the slice's group scale
-// into the split's weight, so one cross-lane read per split gives the factor of its codes.
+// Steps with fewer than 512 rows, 16-bit partials: a quarter row per workgroup (one 128-dim
+// scale group), and every split's codes requested in one round trip. Such rows have many
+// splits (tp8: 240). Wavefront w takes splits w + 4k (k < 64); its lane group g = lane / 16
+// reads split k = 4j + g with load j (j < 16), lane l owning dims 8 (l % 16) .. + 8 of the
+// slice, so a wavefront covers four splits per 16-byte load and a lane has 16 code loads and
+// 16 scalar loads in flight (a one-dword load per split took 64 code loads per lane, over the
+// 63 a wavefront can count, and serialised the last of them). Lane s holds the scalars of
+// splits s, s + 64, s + 128, s + 192 and folds the slice's group scale into the split's
+// weight; each wavefront lays its splits' factors out in LDS so that a lane's 16 are
+// contiguous. The 16 partial sums of each dim (4 wavefronts x 4 lane groups) meet in LDS.
 // A row has at most kMaxSplits = 256 splits (the work list makes at most one item per compute
 // unit, capped at kMaxSplits, and a fixed split count is capped there too).
 __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, Workspace ws) {
-  constexpr int kSlices = kScaleGroups;  // one scale group per workgroup
-  constexpr int kJ = kMaxSplits / kWaves;  // splits per wavefront
-  constexpr int kScal = kMaxSplits / 64;   // split scalars per lane
-  __shared__ float red[kWaves - 1][2][64];
+  constexpr int kSlices = kScaleGroups;       // one scale group per workgroup
+  constexpr int kGroups = 4;                  // lane groups of 16, one split each per load
+  constexpr int kJ = kMaxSplits / (kWaves * kGroups);  // code loads per lane
+  constexpr int kScal = kMaxSplits / 64;      // split scalars per lane
+  constexpr int kDims = 8;                    // dims per lane
+  static_assert(kScaleGroupDims == 16 * kDims, "16 lanes cover a scale group");
+  // factors: wavefront w's split 4k + w at [w][(k % 4) * kJ + k / 4]; sums: [w][g][q][dim]
+  __shared__ __attribute__((aligned(16))) float fac[kWaves][kGroups * kJ];
+  __shared__ __attribute__((aligned(16))) float red[kWaves][kGroups][16][kDims];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);  // the same, in a scalar register
+  const int g = lane >> 4, q = lane & 15;
   const int64_t row = blockIdx.x / kSlices;
   const int slice = int(blockIdx.x % kSlices);
   const int64_t t = row / a.H;
-  const int dim_a = slice * kScaleGroupDims + 2 * lane;
 
   const SegTables tabs = prefetch_tables(a, lane);
   // where this row's partials are (checked to stay inside the workspace, as above)
@@ -441,16 +449,18 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
     base = 0;
     stride = 0;
   }
-  const int16_t *codes = static_cast<const int16_t *>(ws.part_o) + base * kLatent + dim_a;
+  const int16_t *codes = static_cast<const int16_t *>(ws.part_o) + base * kLatent +
+                         slice * kScaleGroupDims + kDims * q;
   const int64_t ostride = stride * kLatent;
   const bool want_arg = a.out_argmax != nullptr;
 
   // every load goes out before the row is validated
-  uint32_t cw[kJ];
+  uint4 cw[kJ];
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
-    const int sp = wave + kWaves * j;
-    cw[j] = sp < S ? *reinterpret_cast<const uint32_t *>(codes + sp * ostride) : 0u;
+    const int sp = kWaves * (kGroups * j + g) + wave;
+    cw[j] = sp < S ? *reinterpret_cast<const uint4 *>(codes + sp * ostride)
+                   : make_uint4(0u, 0u, 0u, 0u);
   }
   float lsv[kScal], mxv[kScal], scv[kScal];
   int32_t agv[kScal];
@@ -480,13 +490,14 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
   } else {
     bad = 8u;
   }
+  // (the same for every wavefront of the workgroup, so all of them return here or none)
   if (!ok) {
     if (threadIdx.x == 0 && slice == 0) {
       atomicOr(ws.status, bad);
       if (a.out_lse) a.out_lse[row] = -INFINITY;
       if (a.out_argmax) a.out_argmax[row] = -1;
     }
-    if (wave == 0) store2(a, row, dim_a, 0.f, 0.f);
+    if (wave == 0) store2(a, row, slice * kScaleGroupDims + 2 * lane, 0.f, 0.f);
     return;
   }
 
@@ -506,41 +517,56 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
     const uint64_t hit = __ballot(mxv[i] == best);
     if (hit) arg = __builtin_amdgcn_readlane(agv[i], int(__builtin_ctzll(hit)));
   }
-  float W = 0.f, acc0 = 0.f, acc1 = 0.f;
-  if (M != -INFINITY) {
-    // per split: its weight, and the weight times the group scale of its codes (zero for a
-    // split without visible keys, whose codes and scale may be unwritten)
-    float wsum = 0.f, f[kScal];
+  // per split: its weight, and the weight times the group scale of its codes (zero for a
+  // split without visible keys, whose codes and scale may be unwritten; zero for every split
+  // when the row sees no key)
+  float wsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < kScal; ++i) {
-      const float w = lsv[i] == -INFINITY ? 0.f : expf(lsv[i] - M);
-      wsum += w;
-      f[i] = w != 0.f ? w * scv[i] : 0.f;
-    }
-    W = wave_sum(wsum);
+  for (int i = 0; i < kScal; ++i) {
+    const float w = lsv[i] == -INFINITY ? 0.f : expf(lsv[i] - M);
+    wsum += w;
+    // split lane + 64 i is split k = lane / 4 + 16 i of wavefront lane % 4
+    if ((lane & 3) == wave)
+      fac[wave][((lane >> 2) & 3) * kJ + (lane >> 4) + 4 * i] = w != 0.f ? w * scv[i] : 0.f;
+  }
+  const float W = M == -INFINITY ? 0.f : wave_sum(wsum);
+  __syncthreads();
+  float fk[kJ];
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      // split wave + 4j: its scalars are in lane (wave + 4j) % 64, slot 4j / 64
-      // (no zero test: a split without weight has a factor of exactly 0 and finite codes)
-      const float fk = lane_f(f[(kWaves * j) / 64], (wv + kWaves * j) & 63);
-      acc0 = fmaf(fk, float(int32_t(cw[j] << 16) >> 16), acc0);
-      acc1 = fmaf(fk, float(int32_t(cw[j]) >> 16), acc1);
+  for (int j4 = 0; j4 < kJ / 4; ++j4) {
+    const float4 v = *reinterpret_cast<const float4 *>(&fac[wave][g * kJ + 4 * j4]);
+    fk[4 * j4] = v.x;
+    fk[4 * j4 + 1] = v.y;
+    fk[4 * j4 + 2] = v.z;
+    fk[4 * j4 + 3] = v.w;
+  }
+  // (no zero test: a split without weight has a factor of exactly 0 and finite codes)
+  float acc[kDims] = {};
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const uint32_t w4[4] = {cw[j].x, cw[j].y, cw[j].z, cw[j].w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc[2 * m] = fmaf(fk[j], float(int32_t(w4[m] << 16) >> 16), acc[2 * m]);
+      acc[2 * m + 1] = fmaf(fk[j], float(int32_t(w4[m]) >> 16), acc[2 * m + 1]);
     }
   }
-  // the four wavefronts' sums meet in LDS; wavefront 0 finishes the slice
-  if (wave > 0) {
-    red[wave - 1][0][lane] = acc0;
-    red[wave - 1][1][lane] = acc1;
-  }
+  *reinterpret_cast<float4 *>(&red[wave][g][q][0]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4 *>(&red[wave][g][q][4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   __syncthreads();
   if (wave != 0) return;
+  // lane l finishes dims 2l, 2l + 1 of the slice: those of lane l / 4 of every group
+  float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-  for (int k = 0; k < kWaves - 1; ++k) {
-    acc0 += red[k][0][lane];
-    acc1 += red[k][1][lane];
-  }
+  for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+    for (int gg = 0; gg < kGroups; ++gg) {
+      const float2 v = *reinterpret_cast<const float2 *>(&red[w][gg][lane >> 2][2 * (lane & 3)]);
+      o0 += v.x;
+      o1 += v.y;
+    }
   const float inv = M == -INFINITY ? 0.f : 1.f / W;
-  store2(a, row, dim_a, acc0 * inv, acc1 * inv);
+  store2(a, row, slice * kScaleGroupDims + 2 * lane, o0 * inv, o1 * inv);
   if (lane == 0 && slice == 0) {
     if (a.out_lse) a.out_lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
     if (a.out_argmax) a.out_argmax[row] = arg;
