@@ -723,23 +723,39 @@ __device__ __forceinline__ void split_range(int L, int k, int n, int &k0, int &k
   k1 = min(L, (t0 + q + (k < r ? 1 : 0)) * kTK);
 }
 
+// Cross-lane sums and maxima over a wavefront without LDS round trips: DPP steps within each
+// 16-lane row (kCtrl: quad_perm 0xB1 = lane ^ 1, 0x4E = lane ^ 2; 0x141 = mirrored within 8
+// lanes, 0x140 = mirrored within 16; each step leaves groups of 2, 4, 8, 16 lanes equal), then
+// the four rows' values read into scalar registers. The result is wave-uniform.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ int64_t dpp_i64(int64_t v) {
+  const uint32_t lo = uint32_t(dpp_i32<kCtrl>(int(uint32_t(uint64_t(v)))));
+  const uint32_t hi = uint32_t(dpp_i32<kCtrl>(int(uint32_t(uint64_t(v) >> 32))));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ int lane_i32(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ int64_t lane_i64(int64_t v, int l) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(uint64_t(v))), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(uint64_t(v) >> 32)), l));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
 __device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_i64<0xB1>(v);
+  v += dpp_i64<0x4E>(v);
+  v += dpp_i64<0x141>(v);
+  v += dpp_i64<0x140>(v);
+  return (lane_i64(v, 0) + lane_i64(v, 16)) + (lane_i64(v, 32) + lane_i64(v, 48));
 }
 __device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  return v;
+  v = max(v, dpp_i32<0xB1>(v));
+  v = max(v, dpp_i32<0x4E>(v));
+  v = max(v, dpp_i32<0x141>(v));
+  v = max(v, dpp_i32<0x140>(v));
+  return max(max(lane_i32(v, 0), lane_i32(v, 16)), max(lane_i32(v, 32), lane_i32(v, 48)));
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ int64_t uniform(int64_t v) {
@@ -866,47 +882,40 @@ __device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan 
     it.prow = 0;
     return true;
   }
+  // Items are numbered request by request: walk this chunk's requests (lane r holds request
+  // base + r) in scalar registers, summing their items and partial rows, to the first whose
+  // items reach past w (item counts are never negative, so that is the request holding w).
   int64_t first = 0, prow = 0;
   for (int base = 0; base < a.bs; base += 64) {
     const ReqWork q = chunk_request<kCached>(a, mine, base, lane);
     const int n = split_count(q, p.c, p.forced);
     const int64_t items = int64_t(q.rt) * n;
     const int64_t prows = int64_t(n) * q.rows;
-    const int64_t si = wave_inclusive_scan64(items, lane);
-    const int64_t sp = wave_inclusive_scan64(prows, lane);
-    const int64_t lo = first + si - items;
-    const uint64_t hit = __ballot(items > 0 && lo <= w && w < lo + items);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      if (lane == l) {
-        const int64_t local = w - lo;
-        it.seg = q.seg;
-        it.rows = q.rows;
-        it.rt = int(local % q.rt);
-        it.k = int(local / q.rt);
-        it.n = n;
-            it.prow = prow + sp - prows;
+    const int nreq = min(a.bs - base, 64);
+    for (int r = 0; r < nreq; ++r) {
+      const int64_t ir = lane_i64(items, r);
+      if (w < first + ir) {  // lane r's values, into scalar registers
+        const int64_t local = w - first;
+        it.seg.q0 = lane_i64(q.seg.q0, r);
+        it.seg.T = lane_i32(q.seg.T, r);
+        it.seg.L = lane_i32(q.seg.L, r);
+        it.seg.P = lane_i32(q.seg.P, r);
+        it.seg.kv0 = lane_i64(q.seg.kv0, r);
+        it.seg.m0 = lane_i64(q.seg.m0, r);
+        // rebuilt from the kernel argument rather than moved between lanes, so that the
+        // compiler still knows it points to global memory (it would otherwise use flat loads)
+        it.seg.tree = a.out_cache_loc ? a.out_cache_loc + it.seg.q0 : nullptr;
+        it.rows = lane_i32(q.rows, r);
+        const int rt = lane_i32(q.rt, r);
+        it.rt = int(local % rt);
+        it.k = int(local / rt);
+        it.n = lane_i32(n, r);
+        it.prow = prow;
+        return true;
       }
-      // lane l's values to every lane (and to scalar registers)
-      it.seg.q0 = __shfl(it.seg.q0, l, 64);
-      it.seg.T = __shfl(it.seg.T, l, 64);
-      it.seg.L = __shfl(it.seg.L, l, 64);
-      it.seg.P = __shfl(it.seg.P, l, 64);
-      it.seg.kv0 = __shfl(it.seg.kv0, l, 64);
-      it.seg.m0 = __shfl(it.seg.m0, l, 64);
-      it.seg = uniform(it.seg);
-      // rebuilt from the kernel argument rather than moved between lanes, so that the
-      // compiler still knows it points to global memory (it would otherwise use flat loads)
-      it.seg.tree = a.out_cache_loc ? a.out_cache_loc + it.seg.q0 : nullptr;
-      it.rows = uniform(__shfl(it.rows, l, 64));
-      it.rt = uniform(__shfl(it.rt, l, 64));
-      it.k = uniform(__shfl(it.k, l, 64));
-      it.n = uniform(__shfl(it.n, l, 64));
-      it.prow = uniform(__shfl(it.prow, l, 64));
-      return true;
+      first += ir;
+      prow += lane_i64(prows, r);
     }
-    first += __shfl(si, 63, 64);
-    prow += __shfl(sp, 63, 64);
   }
   return false;
 }
