@@ -757,6 +757,27 @@ __device__ __forceinline__ int wave_max_int(int v) {
   v = max(v, dpp_i32<0x140>(v));
   return max(max(lane_i32(v, 0), lane_i32(v, 16)), max(lane_i32(v, 32), lane_i32(v, 48)));
 }
+// Inclusive prefix sum over the wavefront's lanes: shifts by 1, 2, 4 and 8 lanes within each
+// 16-lane row (zero where the source lies before the row's start), then the last lane of row
+// 0 and of row 2 added to rows 1 and 3 (row_bcast:15, rows enabled 0b1010), then lane 31's
+// total added to rows 2 and 3 (row_bcast:31, rows 0b1100). 64-bit values move as two halves.
+template <int kCtrl, int kRowMask, bool kBound>
+__device__ __forceinline__ int64_t dpp_scan_src(int64_t v) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(uint64_t(v))), kCtrl,
+                                                           kRowMask, 0xf, kBound));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(uint64_t(v) >> 32)),
+                                                           kCtrl, kRowMask, 0xf, kBound));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
+  v += dpp_scan_src<0x111, 0xf, true>(v);  // row_shr:1
+  v += dpp_scan_src<0x112, 0xf, true>(v);  // row_shr:2
+  v += dpp_scan_src<0x114, 0xf, true>(v);  // row_shr:4
+  v += dpp_scan_src<0x118, 0xf, true>(v);  // row_shr:8
+  v += dpp_scan_src<0x142, 0xa, false>(v);  // row_bcast:15
+  v += dpp_scan_src<0x143, 0xc, false>(v);  // row_bcast:31
+  return v;
+}
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ int64_t uniform(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
@@ -882,40 +903,41 @@ __device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan 
     it.prow = 0;
     return true;
   }
-  // Items are numbered request by request: walk this chunk's requests (lane r holds request
-  // base + r) in scalar registers, summing their items and partial rows, to the first whose
-  // items reach past w (item counts are never negative, so that is the request holding w).
+  // Items are numbered request by request (lane r holds request base + r): the request
+  // holding item w is the one whose range [lo, lo + items) of item numbers contains it, from
+  // prefix sums over the lanes; its values come to scalar registers by lane reads.
   int64_t first = 0, prow = 0;
   for (int base = 0; base < a.bs; base += 64) {
     const ReqWork q = chunk_request<kCached>(a, mine, base, lane);
     const int n = split_count(q, p.c, p.forced);
     const int64_t items = int64_t(q.rt) * n;
     const int64_t prows = int64_t(n) * q.rows;
-    const int nreq = min(a.bs - base, 64);
-    for (int r = 0; r < nreq; ++r) {
-      const int64_t ir = lane_i64(items, r);
-      if (w < first + ir) {  // lane r's values, into scalar registers
-        const int64_t local = w - first;
-        it.seg.q0 = lane_i64(q.seg.q0, r);
-        it.seg.T = lane_i32(q.seg.T, r);
-        it.seg.L = lane_i32(q.seg.L, r);
-        it.seg.P = lane_i32(q.seg.P, r);
-        it.seg.kv0 = lane_i64(q.seg.kv0, r);
-        it.seg.m0 = lane_i64(q.seg.m0, r);
-        // rebuilt from the kernel argument rather than moved between lanes, so that the
-        // compiler still knows it points to global memory (it would otherwise use flat loads)
-        it.seg.tree = a.out_cache_loc ? a.out_cache_loc + it.seg.q0 : nullptr;
-        it.rows = lane_i32(q.rows, r);
-        const int rt = lane_i32(q.rt, r);
-        it.rt = int(local % rt);
-        it.k = int(local / rt);
-        it.n = lane_i32(n, r);
-        it.prow = prow;
-        return true;
-      }
-      first += ir;
-      prow += lane_i64(prows, r);
+    const int64_t si = wave_inclusive_scan64(items);
+    const int64_t sp = wave_inclusive_scan64(prows);
+    const int64_t lo = first + si - items;
+    const uint64_t hit = __ballot(items > 0 && lo <= w && w < lo + items);
+    if (hit) {
+      const int r = __builtin_ctzll(hit);
+      const int64_t local = w - lane_i64(lo, r);
+      it.seg.q0 = lane_i64(q.seg.q0, r);
+      it.seg.T = lane_i32(q.seg.T, r);
+      it.seg.L = lane_i32(q.seg.L, r);
+      it.seg.P = lane_i32(q.seg.P, r);
+      it.seg.kv0 = lane_i64(q.seg.kv0, r);
+      it.seg.m0 = lane_i64(q.seg.m0, r);
+      // rebuilt from the kernel argument rather than moved between lanes, so that the
+      // compiler still knows it points to global memory (it would otherwise use flat loads)
+      it.seg.tree = a.out_cache_loc ? a.out_cache_loc + it.seg.q0 : nullptr;
+      it.rows = lane_i32(q.rows, r);
+      const int rt = lane_i32(q.rt, r);
+      it.rt = int(local % rt);
+      it.k = int(local / rt);
+      it.n = lane_i32(n, r);
+      it.prow = prow + lane_i64(sp - prows, r);
+      return true;
     }
+    first += lane_i64(si, 63);
+    prow += lane_i64(sp, 63);
   }
   return false;
 }
