@@ -79,6 +79,7 @@ class HipEvents:
         self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                 ctypes.c_void_p]
         self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     # timing-only events: no system-scope fence when recorded (its cache writeback would be
     # charged to the kernel being timed); the host synchronises the device before reading them
@@ -97,6 +98,11 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
         return float(f.value)
+
+    def record(self, e, stream_handle):
+        rc = self.rt.hipEventRecord(e, stream_handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def destroy(self, e):
         self.rt.hipEventDestroy(e)
@@ -483,8 +489,8 @@ def summarize_profile(out_dir, workload, dest=None):
         o = [f"# {stem} - workload '{workload}' (bench.py's '{workload}' configuration)", "",
              "Commands (<repo> is the repository root, <out> a scratch folder):"]
         o += ["  " + c for c in profile_commands(workload)]
-        o += ["", f"Kernel trace ({len(d)} dispatches: checked call, warm-up, timed steps, graph "
-                  "replays and cold replays):",
+        o += ["", f"Kernel trace ({len(d)} dispatches: checked call, settle and warm-up steps, "
+                  "timed steps, graph replays and cold replays):",
               "  instantiations: " + ", ".join(names),
               f"  average {statistics.mean(d):.3f} us, median {statistics.median(d):.3f} us, "
               f"min {min(d):.3f} us, max {max(d):.3f} us",
@@ -594,6 +600,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="untimed steps for at least this long before the warm-up steps: the "
+                         "GPU's clock takes about 15-20 ms of load to reach its steady value "
+                         "(reported as settle_steps)")
     ap.add_argument("--workload", default="long", choices=sorted(workload_names()))
     ap.add_argument("--kernel", default="auto", choices=["auto", "simple", "mfma"])
     ap.add_argument("--splits", type=int, default=0)
@@ -676,6 +686,15 @@ def main():
         run_on(stream.cuda_stream)
 
     run_on(stream.cuda_stream, check=True)
+    # settle: untimed steps until the clock has had settle_ms of load (in batches of 16 steps,
+    # each batch waited for, so the count reflects device time)
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(16):
+            step()
+        settle_steps += 16
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -684,22 +703,27 @@ def main():
         log(f"bad output: status={status}")
         sys.exit(1)
 
-    # ---- timed region: K eager steps, per-kernel HIP events recorded by the library
+    # ---- timed region: K eager steps, per-kernel HIP events recorded by the library on the
+    # launch stream: step i records edge[i] ahead of its partial kernel and mid[i] between its
+    # two kernels; edge[i + 1] (the next step's, or one recorded after the last step) ends
+    # its combine. Two events per step rather than three: each recorded event is a queue
+    # packet that costs the step about 1.5 us.
     hev = HipEvents()
-    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(args.steps)]
+    edge = [hev.create() for _ in range(args.steps + 1)]
+    mid = [hev.create() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e in evs:
-        verify_attn_set_profiling_events(va.ctx, *e)
+    for i in range(args.steps):
+        verify_attn_set_profiling_events(va.ctx, edge[i], mid[i], None)
         step()
+    hev.record(edge[args.steps], stream.cuda_stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     verify_attn_set_profiling_events(va.ctx, None, None, None)
-    part_ms = np.array([hev.elapsed_ms(a, b) for a, b, _ in evs])
-    comb_ms = np.array([hev.elapsed_ms(b, c) for _, b, c in evs])
-    for e in evs:
-        for x in e:
-            hev.destroy(x)
+    part_ms = np.array([hev.elapsed_ms(edge[i], mid[i]) for i in range(args.steps)])
+    comb_ms = np.array([hev.elapsed_ms(mid[i], edge[i + 1]) for i in range(args.steps)])
+    for x in edge + mid:
+        hev.destroy(x)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     log(f"eager: {ms_per_step * 1e3:.2f} us/step; partial {part_ms.mean() * 1e3:.2f} us, "
         f"combine {comb_ms.mean() * 1e3:.2f} us")
@@ -777,6 +801,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": False,
         "scaling": "weak",

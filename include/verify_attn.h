@@ -223,8 +223,11 @@ va_status verify_attn_read_device_status(verify_attn_ctx *ctx, void *stream, uin
 
 /* Profiling: when set (non-NULL hipEvent_t handles passed as void*), every later
  * verify_attn_run records `before` ahead of the partial kernel, `between` after it and
- * `after` after the combine kernel, on the run's stream. Pass NULLs to stop. Not for use
- * while the stream is being captured. */
+ * `after` after the combine kernel, on the run's stream. `after` may be NULL with the other
+ * two set: a caller timing back-to-back runs then takes the next run's `before` (or an event
+ * of its own after the last run) as the end of this one, one event fewer per run. Pass NULLs
+ * to stop. Any other combination fails with VA_ERR_INVALID. Not for use while the stream is
+ * being captured. */
 va_status verify_attn_set_profiling_events(verify_attn_ctx *ctx, void *before, void *between,
                                            void *after);
 

@@ -424,8 +424,10 @@ va_status verify_attn_set_profiling_events(verify_attn_ctx *ctx, void *before, v
                                            void *after) {
   if (!ctx) return fail(VA_ERR_NULL, "ctx is NULL");
   const bool all = before && between && after;
+  const bool two = before && between && !after;  // the next run's `before` ends this one
   const bool none = !before && !between && !after;
-  if (!all && !none) return fail(VA_ERR_INVALID, "pass three events or none");
+  if (!all && !two && !none)
+    return fail(VA_ERR_INVALID, "pass three events, `before` and `between`, or none");
   ctx->ev[0] = static_cast<hipEvent_t>(before);
   ctx->ev[1] = static_cast<hipEvent_t>(between);
   ctx->ev[2] = static_cast<hipEvent_t>(after);
