@@ -47,8 +47,7 @@ __device__ __forceinline__ int64_t mask_segment(const TreeArgs &a, int r) {
 __device__ int64_t mask_offset(const TreeArgs &a, int r, int64_t *red) {
   int64_t v = 0;
   for (int k = int(threadIdx.x); k < r; k += kMaskThreads) v += mask_segment(a, k);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum_i64(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   int64_t s = 0;
@@ -146,12 +145,6 @@ __global__ void __launch_bounds__(kMaskThreads) build_mask_kernel(TreeArgs a) {
   for (int k = threadIdx.x; k < T; k += kMaskThreads) row[P + k] = uint8_t(anc[k]);
 }
 
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
 // One wavefront per request.
 __global__ void __launch_bounds__(64) accept_kernel(AcceptArgs a) {
   extern __shared__ int64_t acc_smem[];  // parents, draft and target tokens [max_q_per_req]
@@ -193,7 +186,7 @@ __global__ void __launch_bounds__(64) accept_kernel(AcceptArgs a) {
     int best = 0x7fffffff;
     for (int c = lane; c < T; c += 64)
       if (par[c] == cur && drf[c] == want) best = min(best, c);
-    best = wave_min(best);
+    best = wave_min_i32(best);
     if (best == 0x7fffffff) break;
     cur = best;
     ++len;

@@ -193,6 +193,88 @@ __device__ __forceinline__ int64_t segment_slot(const RunArgs &a, const Segment 
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 hipError_t static_scratch(hipStream_t stream, void **base);
 
+// ---- cross-lane work within a wavefront without LDS round trips (a __shfl is an LDS
+// permute whose result is waited for, so a chain of them serialises on LDS latency)
+//
+// DPP operands (kCtrl): quad_perm 0xB1 = lane ^ 1, 0x4E = lane ^ 2; 0x141 and 0x140 = the
+// lane mirrored within 8 and within 16 lanes; 0x111..0x118 = the lane 1..8 places lower in
+// its 16-lane row (zero, with kBound, where that lies before the row); 0x142 and 0x143 =
+// row_bcast:15 and :31 (the last lane of the row before, and lane 31, into the rows kRowMask
+// enables; disabled rows read zero).
+template <int kCtrl, int kRowMask = 0xf, bool kBound = false>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, kBound);
+}
+template <int kCtrl, int kRowMask = 0xf, bool kBound = false>
+__device__ __forceinline__ int64_t dpp_i64(int64_t v) {
+  const uint32_t lo = uint32_t(dpp_i32<kCtrl, kRowMask, kBound>(int(uint32_t(uint64_t(v)))));
+  const uint32_t hi = uint32_t(dpp_i32<kCtrl, kRowMask, kBound>(int(uint32_t(uint64_t(v) >> 32))));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_i32<kCtrl>(__builtin_bit_cast(int, v)));
+}
+// lane l's value (l wave-uniform), in scalar registers
+__device__ __forceinline__ int lane_i32(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ int64_t lane_i64(int64_t v, int l) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(uint64_t(v))), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(uint64_t(v) >> 32)), l));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+// Wavefront sums, maxima and minima: a butterfly within each 16-lane row (each step leaves
+// groups of 2, 4, 8, 16 lanes equal), then the four rows' values. The result is the same in
+// every lane, and in every wavefront that holds the same values in the same lanes.
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+  v += dpp_i64<0xB1>(v);
+  v += dpp_i64<0x4E>(v);
+  v += dpp_i64<0x141>(v);
+  v += dpp_i64<0x140>(v);
+  return (lane_i64(v, 0) + lane_i64(v, 16)) + (lane_i64(v, 32) + lane_i64(v, 48));
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, dpp_i32<0xB1>(v));
+  v = max(v, dpp_i32<0x4E>(v));
+  v = max(v, dpp_i32<0x141>(v));
+  v = max(v, dpp_i32<0x140>(v));
+  return max(max(lane_i32(v, 0), lane_i32(v, 16)), max(lane_i32(v, 32), lane_i32(v, 48)));
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, dpp_i32<0xB1>(v));
+  v = min(v, dpp_i32<0x4E>(v));
+  v = min(v, dpp_i32<0x141>(v));
+  v = min(v, dpp_i32<0x140>(v));
+  return min(min(lane_i32(v, 0), lane_i32(v, 16)), min(lane_i32(v, 32), lane_i32(v, 48)));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
+}
+// Inclusive prefix sum over the lanes: shifts by 1, 2, 4 and 8 within each 16-lane row, then
+// the last lane of rows 0 and 2 added to rows 1 and 3, then lane 31's total to rows 2 and 3.
+__device__ __forceinline__ int64_t wave_inclusive_scan_i64(int64_t v) {
+  v += dpp_i64<0x111, 0xf, true>(v);
+  v += dpp_i64<0x112, 0xf, true>(v);
+  v += dpp_i64<0x114, 0xf, true>(v);
+  v += dpp_i64<0x118, 0xf, true>(v);
+  v += dpp_i64<0x142, 0xa, false>(v);
+  v += dpp_i64<0x143, 0xc, false>(v);
+  return v;
+}
+
 // Launchers (each defined next to its kernels).
 hipError_t launch_simple_partial(const RunArgs &a, const Workspace &ws, int in_fp32,
                                  hipStream_t st);

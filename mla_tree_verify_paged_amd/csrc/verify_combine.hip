@@ -32,35 +32,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-// Cross-lane moves without LDS round trips: a DPP operand (kCtrl: quad_perm 0xB1 = lane ^ 1,
-// 0x4E = lane ^ 2; 0x141 = mirrored within 8 lanes, 0x140 = mirrored within 16), and lane l's
-// value read into a scalar register (l wave-uniform).
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               kCtrl, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float lane_f(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-// Wavefront max and sum: a butterfly within each 16-lane row (each step leaves groups of 2,
-// 4, 8, 16 lanes equal), then the four rows' values. Every lane gets the same result, and so
-// does every wavefront that holds the same values in the same lanes.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x140>(v));
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  v += dpp<0x140>(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
-}
-
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
@@ -104,11 +75,6 @@ __device__ __forceinline__ SegTables prefetch_tables(const RunArgs &a, int lane)
   }
   return p;
 }
-__device__ __forceinline__ int64_t lane_value(int64_t v, int src) {
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), src));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint64_t(v) >> 32), src));
-  return int64_t((uint64_t(hi) << 32) | lo);
-}
 // The segment of the request that owns token t (the same request owner_request picks) and
 // its VA_DEV_* bits. Wave-uniform.
 __device__ __forceinline__ uint32_t owner_segment(const RunArgs &a, const SegTables &p,
@@ -116,9 +82,9 @@ __device__ __forceinline__ uint32_t owner_segment(const RunArgs &a, const SegTab
   if (a.bs > 64) return load_segment(a, owner_request(a, t, lane), seg);
   const uint64_t le = __ballot(lane < a.bs && p.q0 <= t);
   const int r = le ? 63 - __builtin_clzll(le) : 0;
-  return check_segment(a, lane_value(p.q0, r), lane_value(p.q1, r),
+  return check_segment(a, lane_i64(p.q0, r), lane_i64(p.q1, r),
                        __builtin_amdgcn_readlane(p.k0, r), __builtin_amdgcn_readlane(p.k1, r),
-                       lane_value(p.m0, r), seg);
+                       lane_i64(p.m0, r), seg);
 }
 
 // the 4 output dims [dim0, dim0 + 4) of `row`
@@ -327,8 +293,8 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
       best = fmaxf(best, pmax[int64_t(s) * stride]);
     }
   }
-  M = wave_max(M);
-  best = wave_max(best);
+  M = wave_max_f32(M);
+  best = wave_max_f32(best);
 
   float W = 0.f;
   int arg = -1;
@@ -355,7 +321,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
         if (want_arg) ag = parg[int64_t(s) * stride];
       }
       const float wgt = ls == -INFINITY ? 0.f : expf(ls - M);
-      W += wave_sum(wgt);
+      W += wave_sum_f32(wgt);
       if (arg < 0) {  // wave-uniform: the lowest split holding the largest max score
         const uint64_t hit = __ballot(s < S && mx == best);
         if (hit) arg = __builtin_amdgcn_readlane(ag, int(__builtin_ctzll(hit)));
@@ -374,7 +340,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(RunArgs a, Workspace 
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           const int sl = wv + kWaves * (j0 + j);  // lane of this split within the 64
-          const float wk = lane_f(wgt, sl);
+          const float wk = lane_f32(wgt, sl);
           // a split with zero weight contributes nothing (its row may be unwritten)
           if (s0 + sl < S && wk != 0.f) {
             const float f0 = wk * x[j].scale(0), f1 = wk * x[j].scale(kV - 1);
@@ -508,8 +474,8 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
     M = fmaxf(M, lsv[i]);
     best = fmaxf(best, mxv[i]);
   }
-  M = wave_max(M);
-  best = wave_max(best);
+  M = wave_max_f32(M);
+  best = wave_max_f32(best);
   // the argmax: the lowest split holding the largest max score (split lane + 64 i)
   int arg = -1;
 #pragma unroll
@@ -529,7 +495,7 @@ __global__ void __launch_bounds__(kThreads) combine_few_rows_kernel(RunArgs a, W
     if ((lane & 3) == wave)
       fac[wave][((lane >> 2) & 3) * kJ + (lane >> 4) + 4 * i] = w != 0.f ? w * scv[i] : 0.f;
   }
-  const float W = M == -INFINITY ? 0.f : wave_sum(wsum);
+  const float W = M == -INFINITY ? 0.f : wave_sum_f32(wsum);
   __syncthreads();
   float fk[kJ];
 #pragma unroll
@@ -665,8 +631,8 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(RunArgs a, Works
       best = fmaxf(best, ws.part_max[pr]);
     }
   }
-  M = wave_max(M);
-  best = wave_max(best);
+  M = wave_max_f32(M);
+  best = wave_max_f32(best);
 
   float W = 0.f;
   int arg = -1;
@@ -683,7 +649,7 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(RunArgs a, Works
         ag = sp < S && want_arg ? ws.part_arg[pr] : -1;
       }
       const float wgt = ls == -INFINITY ? 0.f : expf(ls - M);
-      W += wave_sum(wgt);
+      W += wave_sum_f32(wgt);
       if (arg < 0) {  // the lowest split holding the largest max score
         const uint64_t hit = __ballot(sp < S && mx == best);
         if (hit) arg = __builtin_amdgcn_readlane(ag, int(__builtin_ctzll(hit)));
@@ -693,7 +659,7 @@ __global__ void __launch_bounds__(kThreads) combine_rows_kernel(RunArgs a, Works
         if (s0 > 0 || j0 > 0) load(s0 + j0);
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
-          const float wk = lane_f(wgt, j0 + j);
+          const float wk = lane_f32(wgt, j0 + j);
           // a split with zero weight contributes nothing (its codes may be unwritten)
           if (s0 + j0 + j < S && wk != 0.f) {
             const float fa = wk * sa[j], fb = wk * sb[j];

@@ -723,61 +723,6 @@ __device__ __forceinline__ void split_range(int L, int k, int n, int &k0, int &k
   k1 = min(L, (t0 + q + (k < r ? 1 : 0)) * kTK);
 }
 
-// Cross-lane sums and maxima over a wavefront without LDS round trips: DPP steps within each
-// 16-lane row (kCtrl: quad_perm 0xB1 = lane ^ 1, 0x4E = lane ^ 2; 0x141 = mirrored within 8
-// lanes, 0x140 = mirrored within 16; each step leaves groups of 2, 4, 8, 16 lanes equal), then
-// the four rows' values read into scalar registers. The result is wave-uniform.
-template <int kCtrl>
-__device__ __forceinline__ int dpp_i32(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
-}
-template <int kCtrl>
-__device__ __forceinline__ int64_t dpp_i64(int64_t v) {
-  const uint32_t lo = uint32_t(dpp_i32<kCtrl>(int(uint32_t(uint64_t(v)))));
-  const uint32_t hi = uint32_t(dpp_i32<kCtrl>(int(uint32_t(uint64_t(v) >> 32))));
-  return int64_t((uint64_t(hi) << 32) | lo);
-}
-__device__ __forceinline__ int lane_i32(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
-__device__ __forceinline__ int64_t lane_i64(int64_t v, int l) {
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(uint64_t(v))), l));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(uint64_t(v) >> 32)), l));
-  return int64_t((uint64_t(hi) << 32) | lo);
-}
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-  v += dpp_i64<0xB1>(v);
-  v += dpp_i64<0x4E>(v);
-  v += dpp_i64<0x141>(v);
-  v += dpp_i64<0x140>(v);
-  return (lane_i64(v, 0) + lane_i64(v, 16)) + (lane_i64(v, 32) + lane_i64(v, 48));
-}
-__device__ __forceinline__ int wave_max_int(int v) {
-  v = max(v, dpp_i32<0xB1>(v));
-  v = max(v, dpp_i32<0x4E>(v));
-  v = max(v, dpp_i32<0x141>(v));
-  v = max(v, dpp_i32<0x140>(v));
-  return max(max(lane_i32(v, 0), lane_i32(v, 16)), max(lane_i32(v, 32), lane_i32(v, 48)));
-}
-// Inclusive prefix sum over the wavefront's lanes: shifts by 1, 2, 4 and 8 lanes within each
-// 16-lane row (zero where the source lies before the row's start), then the last lane of row
-// 0 and of row 2 added to rows 1 and 3 (row_bcast:15, rows enabled 0b1010), then lane 31's
-// total added to rows 2 and 3 (row_bcast:31, rows 0b1100). 64-bit values move as two halves.
-template <int kCtrl, int kRowMask, bool kBound>
-__device__ __forceinline__ int64_t dpp_scan_src(int64_t v) {
-  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(uint64_t(v))), kCtrl,
-                                                           kRowMask, 0xf, kBound));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(uint64_t(v) >> 32)),
-                                                           kCtrl, kRowMask, 0xf, kBound));
-  return int64_t((uint64_t(hi) << 32) | lo);
-}
-__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
-  v += dpp_scan_src<0x111, 0xf, true>(v);  // row_shr:1
-  v += dpp_scan_src<0x112, 0xf, true>(v);  // row_shr:2
-  v += dpp_scan_src<0x114, 0xf, true>(v);  // row_shr:4
-  v += dpp_scan_src<0x118, 0xf, true>(v);  // row_shr:8
-  v += dpp_scan_src<0x142, 0xa, false>(v);  // row_bcast:15
-  v += dpp_scan_src<0x143, 0xc, false>(v);  // row_bcast:31
-  return v;
-}
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ int64_t uniform(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
@@ -810,7 +755,7 @@ __device__ int64_t count_items(const RunArgs &a, const ReqWork &mine, int c, int
   int64_t n = 0;
   for (int base = 0; base < a.bs; base += 64) {
     const ReqWork q = chunk_request<true>(a, mine, base, lane);
-    n += wave_sum64(int64_t(q.rt) * split_count(q, c, forced));
+    n += wave_sum_i64(int64_t(q.rt) * split_count(q, c, forced));
   }
   return uniform(n);
 }
@@ -832,9 +777,9 @@ __device__ WorkPlan plan_work(const RunArgs &a, const ReqWork &mine, int G, int 
     for (int base = 0; base < a.bs; base += 64) {
       const ReqWork q = chunk_request<true>(a, mine, base, lane);
       if (report && q.bad) atomicOr(status, q.bad);
-      C += wave_sum64(int64_t(q.rt) * q.kt);
-      RT += wave_sum64(int64_t(q.rt));
-      ktmax = max(ktmax, wave_max_int(q.kt));
+      C += wave_sum_i64(int64_t(q.rt) * q.kt);
+      RT += wave_sum_i64(int64_t(q.rt));
+      ktmax = max(ktmax, wave_max_i32(q.kt));
     }
     C = uniform(C);
     RT = uniform(RT);
@@ -912,8 +857,8 @@ __device__ bool find_item(const RunArgs &a, const ReqWork &mine, const WorkPlan 
     const int n = split_count(q, p.c, p.forced);
     const int64_t items = int64_t(q.rt) * n;
     const int64_t prows = int64_t(n) * q.rows;
-    const int64_t si = wave_inclusive_scan64(items);
-    const int64_t sp = wave_inclusive_scan64(prows);
+    const int64_t si = wave_inclusive_scan_i64(items);
+    const int64_t sp = wave_inclusive_scan_i64(prows);
     const int64_t lo = first + si - items;
     const uint64_t hit = __ballot(items > 0 && lo <= w && w < lo + items);
     if (hit) {
