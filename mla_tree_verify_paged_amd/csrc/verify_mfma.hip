@@ -110,8 +110,6 @@ __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
-
 // The value lane l ^ 32 holds (v_permlane32_swap, no LDS round trip).
 __device__ __forceinline__ int other_half(int v) {
   const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
@@ -1114,7 +1112,7 @@ __device__ __forceinline__ void run_item(const RunArgs &a, const Workspace &ws, 
   // ---- write the partial of this split
   if (!active) return;
   matrix_drain();
-  const float ltot = st.lsum + swap_halves(st.lsum);
+  const float ltot = st.lsum + other_half(st.lsum);
   if (!row_ok) return;
   const int64_t prow = it.prow + int64_t(it.k) * rows_req + rho;
   if (prow >= ws.part_rows) {  // cannot happen: the workspace is sized for every plan
@@ -1396,7 +1394,7 @@ __device__ __forceinline__ void run_narrow(const RunArgs &a, const Workspace &ws
   // ---- write this wavefront's 128 dims of the split's partial (and, from wavefront 0, the
   // row's scalars and placement)
   matrix_drain();
-  const float ltot = st.lsum + swap_halves(st.lsum);
+  const float ltot = st.lsum + other_half(st.lsum);
   if (!row_ok) return;
   const int64_t prow = it.prow + int64_t(it.k) * rows_req + rho;
   if (prow >= ws.part_rows) {  // cannot happen: the workspace is sized for every plan
@@ -1795,7 +1793,7 @@ __device__ __forceinline__ void ws_score(const RunArgs &a, const Workspace &ws, 
   }
   __syncthreads();  // every P has been taken: the exchange area is free
 
-  const float ltot = st.lsum + swap_halves(st.lsum);
+  const float ltot = st.lsum + other_half(st.lsum);
   float ma = 0.f;  // this wavefront's part of the shared scale group
   if constexpr (kSplit) ma = lane_absmax<kABlocks - 4 * kSplitG>(o + 4 * kSplitG);
   if (w.active) {
