@@ -453,6 +453,22 @@ def _bench_line(path):
     return json.loads(lines[-1]) if lines else {}
 
 
+def _timed_dispatches(d, bench, stem):
+    """The trace average over the traced run's timed steps alone, for the kernels every step
+    launches once (the partial and combine kernels): the dispatches after the checked call,
+    the settle steps and the warm-up. The all-dispatch average above mixes the clock's ramp
+    and the graph and cold replays in."""
+    if not bench or not ("partial" in stem or "combine" in stem):
+        return []
+    s0 = 1 + int(bench.get("settle_steps", 0)) + int(bench.get("warmup", 0))
+    k = int(bench.get("steps", 0))
+    if k <= 0 or len(d) < s0 + k:
+        return []
+    t = d[s0:s0 + k]
+    return [f"  the {k} timed steps (dispatches {s0}..{s0 + k - 1}): average "
+            f"{sum(t) / k:.3f} us, min {min(t):.3f} us, max {max(t):.3f} us"]
+
+
 def summarize_profile(out_dir, workload, dest=None):
     """Writes profiles/<kernel>_<workload>.txt for every profiled kernel that ran: its kernel
     trace and --stats row, and its HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE
@@ -489,11 +505,14 @@ def summarize_profile(out_dir, workload, dest=None):
         o = [f"# {stem} - workload '{workload}' (bench.py's '{workload}' configuration)", "",
              "Commands (<repo> is the repository root, <out> a scratch folder):"]
         o += ["  " + c for c in profile_commands(workload)]
-        o += ["", f"Kernel trace ({len(d)} dispatches: checked call, settle and warm-up steps, "
-                  "timed steps, graph replays and cold replays):",
+        what = ("checked call, settle and warm-up steps, timed steps, graph replays and cold "
+                "replays" if ("partial" in stem or "combine" in stem) else
+                "the tree-op timing's checked calls, warm-up and graph replays")
+        o += ["", f"Kernel trace ({len(d)} dispatches: {what}):",
               "  instantiations: " + ", ".join(names),
               f"  average {statistics.mean(d):.3f} us, median {statistics.median(d):.3f} us, "
               f"min {min(d):.3f} us, max {max(d):.3f} us",
+              *_timed_dispatches(d, bench, stem),
               f"  grid {r0['Grid_Size_X']} work-items, workgroup {r0['Workgroup_Size_X']}, LDS "
               f"{r0['LDS_Block_Size']} B, VGPR {r0['VGPR_Count']}, AGPR "
               f"{r0['Accum_VGPR_Count']}, SGPR {r0['SGPR_Count']}, scratch {r0['Scratch_Size']} B",
