@@ -94,7 +94,7 @@ typedef enum {
   VA_OK = 0,
   VA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
   VA_ERR_INVALID = 2,     /* a scalar is out of range or inconsistent with the config      */
-  VA_ERR_UNSUPPORTED = 3, /* a valid request this build does not implement                */
+  VA_ERR_UNSUPPORTED = 3, /* a valid request the library does not implement              */
   VA_ERR_WORKSPACE = 4,   /* the caller's workspace is too small or misaligned            */
   VA_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed                   */
 } va_status;
