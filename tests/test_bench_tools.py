@@ -85,3 +85,17 @@ def test_summarize_profile_scales_the_byte_counters(tmp_path):
     assert "average 71.000 us, median 71.000 us" in text
     assert "calls 2, average 71.000 us" in text
     assert "bench.py --workload long --summarize-profile <out>" in text
+
+
+def test_timed_dispatches_slice_after_the_settle_and_warmup_steps():
+    # 1 checked call, 3 settle steps, 2 warm-up steps, then 4 timed steps, then replays
+    d = [50.0] + [80.0] * 3 + [70.0] * 2 + [60.0, 62.0, 64.0, 66.0] + [90.0] * 5
+    line = bench._timed_dispatches(d, {"settle_steps": 3, "warmup": 2, "steps": 4},
+                                   "mfma_partial_ws_kernel")
+    assert line == ["  the 4 timed steps (dispatches 6..9): average 63.000 us, min 60.000 us, "
+                    "max 66.000 us"]
+    # the tree kernels are not launched once per step; too few dispatches give nothing either
+    assert bench._timed_dispatches(d, {"settle_steps": 3, "warmup": 2, "steps": 4},
+                                   "build_mask_kernel") == []
+    assert bench._timed_dispatches(d[:8], {"settle_steps": 3, "warmup": 2, "steps": 4},
+                                   "combine_kernel") == []

@@ -439,6 +439,26 @@ def test_split_counts_agree(kernel):
         assert d <= tol
 
 
+@pytest.mark.parametrize("shape,splits", [
+    ("few_rows", 1), ("few_rows", 5), ("few_rows", 13), ("few_rows", 64), ("few_rows", 65),
+    ("few_rows", 256), ("rows1024", 3), ("rows1024", 13), ("rows1024", 33), ("rows3072", 3),
+    ("rows3072", 7)])
+def test_combine_shapes_over_split_counts(shape, splits):
+    """Each merge kernel over fixed split counts against the oracle: the few-rows merge (32
+    rows, H = 8; split counts that leave lane groups partly empty, more than 64 splits so lanes
+    hold several splits' scalars, and 256 capped at the 188 key tiles), the one-workgroup-per-row
+    merge (1024 rows) and the one-wavefront-per-row merge (3072 rows)."""
+    if shape == "few_rows":
+        w = wl.build_workload("cs", np.random.default_rng(60 + splits), 8, [6000], [4], 16384)
+    elif shape == "rows1024":
+        w = wl.build_workload("cs", np.random.default_rng(70 + splits), 64, [3000], [16], 16384)
+    else:
+        w = wl.build_workload("cs", np.random.default_rng(80 + splits), 64, [2000, 1500],
+                              [32, 16], 16384)
+    say(f"{shape}, {splits} splits")
+    ref = run_oracle(w)
+    compare(w, run_gpu(w, kernel="mfma", num_splits=splits), ref)
+
 # ----------------------------------------------------------------------------- value range
 @pytest.mark.parametrize("shape", ["rows1024", "rows24"])
 def test_latent_values_beyond_fp16_saturate_as_documented(shape):
